@@ -1,0 +1,321 @@
+// CPU oracle for NVFP4 block-scaled quantization (rtn6 and Four Over Six).
+//
+// TEST INFRASTRUCTURE ONLY -- loaded by the tests, the smoke check and the benchmark's
+// CPU-baseline leg, never by the product path.  No code is shared with the HIP library.
+// Build: g++ -std=c++17 -O2 -ffp-contract=off -fPIC -shared (no fast-math).
+//
+// Readings of the pages that this file fixes (the pages are silent on them) are marked
+// "reading:".  Everything else states what the pages define.
+#include "nvfp4_oracle.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+std::atomic<int64_t> g_inexact{0};
+
+float f32_from_bits(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
+uint32_t bits_from_f32(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
+float bf16_value(uint16_t h) { return f32_from_bits(uint32_t(h) << 16); }
+
+// The FP4 (E2M1) value set: 0, 0.5, 1, 1.5, 2, 3, 4, 6 -- steps of 0.5 on [0,2], 1 on
+// [2,4] and 2 on [4,6] [4/6, lay section on the problem; "Problem definition"].  Index =
+// 3-bit magnitude code e1 e0 m (exponent bias 1, e = 0 is the subnormal 0.5*m).
+const double kE2M1Mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+// Nearest E2M1 magnitude by exact distance.  reading: ties go to the even code (IEEE RNE:
+// the code whose mantissa bit is 0); values above 6 saturate to 6 (FP4 has no infinity).
+int e2m1_round_mag(float a) {
+  if (a >= 6.0f) return 7;                       // saturation, an explicit clamp
+  const double ad = a;
+  int best = 0;
+  double bestd = std::fabs(ad - kE2M1Mag[0]);
+  for (int c = 1; c < 8; ++c) {
+    const double dist = std::fabs(ad - kE2M1Mag[c]);
+    // a tie is between neighbours c-1 and c: keep whichever code is even
+    if (dist < bestd || (dist == bestd && (c & 1) == 0)) { best = c; bestd = dist; }
+  }
+  return best;
+}
+
+// E4M3FN byte -> exact value: sign, 4-bit exponent (bias 7), 3-bit mantissa; exponent
+// field 0 is subnormal m * 2^-9; 0x7E = 448 is the largest finite value, 0x7F is NaN.
+// The block scale is FP8 E4M3 with largest value 448 [4/6, "Implementation details"].
+double e4m3_value(int b) {
+  const int e = (b >> 3) & 0xF, m = b & 7;
+  const double mag = e == 0 ? std::ldexp(double(m), -9) : std::ldexp(1.0 + m / 8.0, e - 7);
+  return (b & 0x80) ? -mag : mag;
+}
+
+// Nearest non-negative finite E4M3 value by exact distance.  reading: RNE (ties to the
+// even byte), saturating at 448 instead of producing NaN, subnormal scales kept.
+int e4m3_encode(float sigma) {
+  const double s = sigma > 448.0f ? 448.0 : double(sigma);
+  int best = 0;
+  double bestd = std::fabs(s - e4m3_value(0));
+  for (int b = 1; b <= 0x7E; ++b) {
+    const double dist = std::fabs(s - e4m3_value(b));
+    if (dist < bestd || (dist == bestd && (b & 1) == 0)) { best = b; bestd = dist; }
+  }
+  return best;
+}
+
+// Value of a bfloat16 pattern (1 sign, 8 exponent bits, bias 127, 7 mantissa bits).  The
+// all-ones exponent with a zero mantissa stands for 2^128 here, the value IEEE rounding
+// compares against before it overflows to infinity.
+double bf16_pattern_value(uint16_t p) {
+  const int e = (p >> 7) & 0xFF, m = p & 0x7F;
+  const double mag = e == 0 ? std::ldexp(double(m), -133) : std::ldexp(1.0 + m / 128.0, e - 127);
+  return (p & 0x8000) ? -mag : mag;
+}
+
+// binary32 -> bfloat16 (finite input), nearest by exact distance, ties to the even pattern.
+uint16_t bf16_rne(float f) {
+  const uint32_t u = bits_from_f32(f);
+  const uint16_t lo = uint16_t(u >> 16);         // truncation toward zero
+  const uint16_t hi = uint16_t(lo + 1);          // next bfloat16 away from zero
+  const double dl = std::fabs(double(f) - bf16_pattern_value(lo));
+  const double dh = std::fabs(double(f) - bf16_pattern_value(hi));
+  if (dl < dh) return lo;
+  if (dh < dl) return hi;
+  return (lo & 1) ? hi : lo;
+}
+
+float alpha_of(float amax, int mode) {
+  // alpha maps the tensor amax to (largest FP4 value 6) x (largest block-scale value M);
+  // Four Over Six uses M = 256 instead of 448 so the 1.5x larger scale of blocks scaled
+  // to 4 cannot overflow E4M3 [4/6, "Implementation details"].  reading: alpha =
+  // amax / (6*M), one binary32 division by the exact constant 2688 or 1536.
+  const float C = mode == ORC_FOUR_OVER_SIX ? 1536.0f : 2688.0f;
+  return amax / C;
+}
+
+struct Candidate {
+  uint8_t scale;
+  uint8_t mag[16];
+  float xhat[16];
+  float err;
+};
+
+// One candidate target block maximum Q (6, or 4 under Four Over Six): scale the block so
+// its max maps to Q, round every value to FP4, dequantize, and measure the error against
+// the original values [4/6, "Adaptive block scaling algorithm": quantize twice, compute
+// both errors against the original high-precision values].
+void run_candidate(const float x[16], float bmax, float alpha, int Q, int rule, Candidate* c) {
+  // reading: block scale sigma = bmax / RN32(Q*alpha), then E4M3 (RNE, saturating).
+  const float cq = float(Q) * alpha;
+  const float sigma = alpha == 0.0f ? 0.0f : bmax / cq;
+  c->scale = uint8_t(e4m3_encode(sigma));
+  // reading: the block's dequantization step d = RN32(dec(s) * alpha).
+  const float d = float(e4m3_value(c->scale)) * alpha;
+  // A block scaled to 4 lives in [-4, 4] and gives up 5 and 6 [4/6, "core mechanism"]:
+  // its magnitude code is capped at 4 (code 6).  Scale 6 keeps the full grid (code 7).
+  const int cap = Q == 4 ? 6 : 7;
+  // reading: values are scaled by the correctly rounded reciprocal r = RN32(1/d) and
+  // v = RN32(x*r); when 1/d overflows binary32 (d <= 2^-128), v = RN32(x/d) instead.
+  // A zero step (scale byte 0) quantizes every value to a (signed) zero code.
+  const float r = d == 0.0f ? 0.0f : 1.0f / d;
+  const bool recip_finite = std::isfinite(r);
+  for (int i = 0; i < 16; ++i) {
+    int m = 0;
+    if (d != 0.0f) {
+      const float v = recip_finite ? x[i] * r : x[i] / d;
+      m = std::min(e2m1_round_mag(std::fabs(v)), cap);
+    }
+    c->mag[i] = uint8_t(m);
+    const float mag_hat = float(kE2M1Mag[m]) * d;       // RN32(val(m) * d)
+    c->xhat[i] = std::signbit(x[i]) ? -mag_hat : mag_hat;
+  }
+  // reading: errors are sums (the 1/16 of a mean never changes which candidate wins),
+  // accumulated sequentially over i = 0..15 in binary32: fma for the squared error, an
+  // add for the absolute error, an exact max for the max error.
+  float acc = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    const float e = x[i] - c->xhat[i];
+    if (double(x[i]) - double(c->xhat[i]) != double(e)) g_inexact.fetch_add(1);
+    if (rule == ORC_MSE)      acc = std::fma(e, e, acc);
+    else if (rule == ORC_MAE) acc = acc + std::fabs(e);
+    else                      acc = std::max(acc, std::fabs(e));
+  }
+  c->err = acc;
+}
+
+void quantize_block(const float x[16], float alpha, int mode, int rule, uint8_t codes8[8],
+                    uint8_t* scale, uint16_t y16[16], orc_block_debug* dbg) {
+  if (std::isnan(alpha)) {                        // poisoned tensor (non-finite input)
+    std::memset(codes8, 0, 8);
+    *scale = 0x7F;
+    if (y16) for (int i = 0; i < 16; ++i) y16[i] = 0x7FC0;
+    if (dbg) { dbg->qstar = 0; dbg->s6 = dbg->s4 = 0x7F; dbg->err6 = dbg->err4 = NAN; }
+    return;
+  }
+  float bmax = 0.0f;                              // block max |x|, exact
+  for (int i = 0; i < 16; ++i) bmax = std::max(bmax, std::fabs(x[i]));
+
+  Candidate c6, c4;
+  run_candidate(x, bmax, alpha, 6, rule, &c6);     // standard NVFP4: block max -> 6
+  const Candidate* win = &c6;
+  if (mode == ORC_FOUR_OVER_SIX) {
+    run_candidate(x, bmax, alpha, 4, rule, &c4);   // Four Over Six: also block max -> 4
+    // keep the scale with the smaller error; reading: a tie keeps 6
+    if (c4.err < c6.err) win = &c4;
+  }
+  *scale = win->scale;
+  for (int j = 0; j < 8; ++j) {
+    // reading: code = sign of x (bit 3, also for zero magnitudes) | magnitude; two codes
+    // per byte, the even element in the low nibble.
+    const int lo = (std::signbit(x[2 * j]) ? 8 : 0) | win->mag[2 * j];
+    const int hi = (std::signbit(x[2 * j + 1]) ? 8 : 0) | win->mag[2 * j + 1];
+    codes8[j] = uint8_t(lo | (hi << 4));
+  }
+  // simulated quantization output: the dequantized value rounded to bf16
+  if (y16) for (int i = 0; i < 16; ++i) y16[i] = bf16_rne(win->xhat[i]);
+  if (dbg) {
+    dbg->qstar = win == &c4 ? 4 : 6;
+    dbg->s6 = c6.scale;
+    dbg->err6 = c6.err;
+    dbg->s4 = mode == ORC_FOUR_OVER_SIX ? c4.scale : 0;
+    dbg->err4 = mode == ORC_FOUR_OVER_SIX ? c4.err : NAN;
+  }
+}
+
+// amax over n elements; NaN if any element is NaN or infinite.
+float tensor_amax(const uint16_t* in, int64_t n) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    const float x = bf16_value(in[i]);
+    if (!std::isfinite(x)) return NAN;
+    amax = std::max(amax, std::fabs(x));
+  }
+  return amax;
+}
+
+template <class F>
+void parallel_ranges(int64_t n, int nthreads, F&& fn) {
+  if (nthreads <= 1 || n < 2) { fn(int64_t(0), n); return; }
+  std::vector<std::thread> ts;
+  const int64_t chunk = (n + nthreads - 1) / nthreads;
+  for (int t = 0; t < nthreads; ++t) {
+    const int64_t lo = t * chunk, hi = std::min(n, lo + chunk);
+    if (lo >= hi) break;
+    ts.emplace_back([&fn, lo, hi] { fn(lo, hi); });
+  }
+  for (auto& t : ts) t.join();
+}
+
+bool bad_args(const void* in, int64_t E, int64_t rows, int64_t cols, int mode, int rule) {
+  return !in || E <= 0 || rows <= 0 || cols <= 0 || cols % 16 != 0 ||
+         (mode != ORC_RTN6 && mode != ORC_FOUR_OVER_SIX) ||
+         (rule != ORC_MSE && rule != ORC_MAE && rule != ORC_MAXERR);
+}
+
+}  // namespace
+
+extern "C" {
+
+float orc_e2m1_decode(int code) {
+  const float mag = float(kE2M1Mag[code & 7]);
+  return (code & 8) ? -mag : mag;
+}
+int orc_e2m1_round_mag(float a) { return e2m1_round_mag(a); }
+void orc_e2m1_round_mag_many(const float* a, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = uint8_t(e2m1_round_mag(a[i]));
+}
+double orc_e4m3_decode(int byte) { return e4m3_value(byte); }
+int orc_e4m3_encode(float sigma) { return e4m3_encode(sigma); }
+void orc_e4m3_encode_many(const float* s, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = uint8_t(e4m3_encode(s[i]));
+}
+uint16_t orc_bf16_rne(float f) { return bf16_rne(f); }
+void orc_bf16_rne_many(const float* f, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_rne(f[i]);
+}
+float orc_alpha(float amax, int mode) { return alpha_of(amax, mode); }
+
+int orc_amax(const uint16_t* in, int64_t E, int64_t n, float* amax_out) {
+  if (!in || !amax_out || E <= 0 || n <= 0) return -1;
+  for (int64_t t = 0; t < E; ++t) amax_out[t] = tensor_amax(in + t * n, n);
+  return 0;
+}
+
+void orc_quantize_block(const uint16_t* x16, float alpha, int mode, int rule, uint8_t* codes8,
+                        uint8_t* scale, uint16_t* y16, orc_block_debug* dbg) {
+  float x[16];
+  for (int i = 0; i < 16; ++i) x[i] = bf16_value(x16[i]);
+  quantize_block(x, alpha, mode, rule, codes8, scale, y16, dbg);
+}
+
+void orc_candidate(const uint16_t* x16, float alpha, int Q, int rule, uint8_t* mag16,
+                   uint8_t* scale, float* xhat16, float* err) {
+  float x[16], bmax = 0.0f;
+  for (int i = 0; i < 16; ++i) { x[i] = bf16_value(x16[i]); bmax = std::max(bmax, std::fabs(x[i])); }
+  Candidate c;
+  run_candidate(x, bmax, alpha, Q == 4 ? 4 : 6, rule, &c);
+  std::memcpy(mag16, c.mag, 16);
+  *scale = c.scale;
+  std::memcpy(xhat16, c.xhat, sizeof c.xhat);
+  *err = c.err;
+}
+
+int orc_quantize(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int mode, int rule,
+                 uint8_t* codes, uint8_t* scales, float* alpha, uint16_t* y, uint8_t* qstar,
+                 int nthreads) {
+  if (bad_args(in, E, rows, cols, mode, rule) || !codes || !scales || !alpha) return -1;
+  const int64_t n = rows * cols, nb = n / 16;
+  for (int64_t t = 0; t < E; ++t) {
+    const uint16_t* x = in + t * n;
+    // pass 1: the tensor amax (combined over ranges by max, which is exact)
+    std::vector<float> part(std::max(1, nthreads), 0.0f);
+    std::atomic<bool> nonfinite{false};
+    std::atomic<int> slot{0};
+    parallel_ranges(n, nthreads, [&](int64_t lo, int64_t hi) {
+      const float a = tensor_amax(x + lo, hi - lo);
+      if (std::isnan(a)) nonfinite = true; else part[slot++] = a;
+    });
+    float amax = 0.0f;
+    for (float a : part) amax = std::max(amax, a);
+    const float al = nonfinite ? NAN : alpha_of(amax, mode);
+    alpha[t] = al;
+    // pass 2: every block with the tensor's alpha
+    parallel_ranges(nb, nthreads, [&](int64_t lo, int64_t hi) {
+      for (int64_t b = lo; b < hi; ++b) {
+        orc_block_debug dbg;
+        float xb[16];
+        for (int i = 0; i < 16; ++i) xb[i] = bf16_value(x[b * 16 + i]);
+        quantize_block(xb, al, mode, rule, codes + (t * nb + b) * 8, scales + t * nb + b,
+                       y ? y + (t * nb + b) * 16 : nullptr, &dbg);
+        if (qstar) qstar[t * nb + b] = uint8_t(dbg.qstar);
+      }
+    });
+  }
+  return 0;
+}
+
+int orc_quantize_blocks(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int mode,
+                        int rule, const float* alpha, const int64_t* ids, int64_t nsel,
+                        uint8_t* codes, uint8_t* scales, uint16_t* y, uint8_t* qstar) {
+  if (bad_args(in, E, rows, cols, mode, rule) || !alpha || !ids || nsel < 0 || !codes ||
+      !scales)
+    return -1;
+  const int64_t nb = rows * cols / 16;
+  for (int64_t k = 0; k < nsel; ++k) {
+    const int64_t b = ids[k];
+    if (b < 0 || b >= E * nb) return -2;
+    float xb[16];
+    for (int i = 0; i < 16; ++i) xb[i] = bf16_value(in[b * 16 + i]);
+    orc_block_debug dbg;
+    quantize_block(xb, alpha[b / nb], mode, rule, codes + k * 8, scales + k,
+                   y ? y + k * 16 : nullptr, &dbg);
+    if (qstar) qstar[k] = uint8_t(dbg.qstar);
+  }
+  return 0;
+}
+
+int64_t orc_inexact_subtractions(void) { return g_inexact.load(); }
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+/*
+ * CPU oracle for NVFP4 block-scaled quantization (standard "rtn6" and Four Over Six).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or call this
+ * code: only the tests, the smoke check and the benchmark's CPU-baseline leg load it.  It
+ * shares no source, header, table or constant with the HIP library.
+ *
+ * Sources (cited by page title and section):
+ *   [4/6]  "Four Over Six: More Accurate NVFP4 Quantization with Adaptive Block Scaling"
+ *          (gist.science explainer): "Problem definition", "Method / core mechanism",
+ *          "Adaptive block scaling algorithm", "Implementation details".
+ *   [QAD]  "Quantization-Aware Distillation for NVFP4 Inference Accuracy Recovery"
+ *          (gist.science explainer), key findings item 3 (NVFP4 block size 16).
+ *   [LTN]  Nemotron 3.5 Lightning NVFP4 news page, "two-stage QAD process" (student forward
+ *          runs through simulated quantization).
+ *
+ * Every floating-point step is one IEEE binary32 operation with round-to-nearest-even,
+ * no contraction (built with -ffp-contract=off), no flush-to-zero; std::fma only where the
+ * spec says fma.  E2M1, E4M3 and bfloat16 rounding are done by brute force: the nearest
+ * grid value by exact binary64 distance, ties to the even code.
+ */
+#ifndef NVFP4_ORACLE_H
+#define NVFP4_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_RTN6 = 0, ORC_FOUR_OVER_SIX = 1 };
+enum { ORC_MSE = 0, ORC_MAE = 1, ORC_MAXERR = 2 };
+
+/* Element and scale formats. */
+float    orc_e2m1_decode(int code);              /* 4-bit code s|e1 e0|m -> value */
+int      orc_e2m1_round_mag(float a);            /* a >= 0 (not NaN) -> magnitude code 0..7 */
+void     orc_e2m1_round_mag_many(const float* a, int64_t n, uint8_t* out);
+double   orc_e4m3_decode(int byte);              /* E4M3FN byte (not 0x7F/0xFF) -> value */
+int      orc_e4m3_encode(float sigma);           /* sigma >= 0 -> byte 0x00..0x7E (saturating) */
+void     orc_e4m3_encode_many(const float* s, int64_t n, uint8_t* out);
+uint16_t orc_bf16_rne(float f);                  /* binary32 -> bfloat16, RNE (finite f) */
+void     orc_bf16_rne_many(const float* f, int64_t n, uint16_t* out);
+
+/* Per-tensor scale alpha = RN32(amax / (6*M)), M = 448 (rtn6) or 256 (four over six). */
+float    orc_alpha(float amax, int mode);
+
+/* Tensor amax of E tensors of n elements each, as binary32; NaN if any element is not finite. */
+int      orc_amax(const uint16_t* in, int64_t E, int64_t n, float* amax_out);
+
+/* Quantize one 16-element block given the tensor's alpha.  Outputs: 8 packed code bytes,
+ * the chosen scale byte, the 16 dequantized values rounded to bf16 (fake-quant), and
+ * debug values: chosen candidate Q (6 or 4), each candidate's scale byte and error (the
+ * 4-candidate fields are 0 / NaN in rtn6 mode). */
+typedef struct {
+  int      qstar;
+  uint8_t  s6, s4;
+  float    err6, err4;
+} orc_block_debug;
+void     orc_quantize_block(const uint16_t* x16, float alpha, int mode, int rule,
+                            uint8_t* codes8, uint8_t* scale, uint16_t* y16,
+                            orc_block_debug* dbg);
+
+/* One candidate alone (Q = 6 or 4) with the given alpha: magnitude codes (16 bytes, 0..7,
+ * sign not included), scale byte, dequantized binary32 values and the error under rule. */
+void     orc_candidate(const uint16_t* x16, float alpha, int Q, int rule, uint8_t* mag16,
+                       uint8_t* scale, float* xhat16, float* err);
+
+/* Whole tensors: in is [E][rows][cols] bf16, cols % 16 == 0.  codes [E][rows][cols/2],
+ * scales [E][rows][cols/16], alpha [E]; y (fake-quant bf16, [E][rows][cols]) and qstar
+ * ([E][rows][cols/16], 6 or 4) may be NULL.  nthreads >= 1 splits each tensor's blocks
+ * into contiguous ranges; the result does not depend on it.  Returns 0 or a negative
+ * error for bad arguments. */
+int      orc_quantize(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int mode,
+                      int rule, uint8_t* codes, uint8_t* scales, float* alpha, uint16_t* y,
+                      uint8_t* qstar, int nthreads);
+
+/* Selected blocks only (for sampled checks at full size): flat block ids over
+ * [E][rows][cols/16]; alpha[E] from orc_amax + orc_alpha (NaN = poisoned tensor). */
+int      orc_quantize_blocks(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
+                             int mode, int rule, const float* alpha, const int64_t* ids,
+                             int64_t nsel, uint8_t* codes, uint8_t* scales, uint16_t* y,
+                             uint8_t* qstar);
+
+/* Count of error subtractions e = x - xhat that were not exact (expected 0). */
+int64_t  orc_inexact_subtractions(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
