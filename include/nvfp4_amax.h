@@ -1,0 +1,139 @@
+/*
+ * nvfp4_amax -- NVFP4 block-scaled quantization of bf16 tensors on AMD Instinct MI355X
+ * (gfx950): standard NVFP4 ("rtn6") and Four Over Six ("4/6") adaptive block scaling,
+ * as a packed quantizer and as a simulated-quantization (quantize-dequantize) op.
+ *
+ * What is computed (sources cited by page title and section):
+ *   - Elements are FP4 E2M1 codes with values {0, 0.5, 1, 1.5, 2, 3, 4, 6} and a sign
+ *     ("Four Over Six: More Accurate NVFP4 Quantization with Adaptive Block Scaling",
+ *     gist.science explainer, "Problem definition").
+ *   - One FP8 E4M3 scale per block of 16 consecutive elements ("Quantization-Aware
+ *     Distillation for NVFP4 Inference Accuracy Recovery", gist.science explainer, key
+ *     findings item 3; Four Over Six explainer, "Implementation details").
+ *   - One FP32 scale alpha per tensor, from the tensor's absolute maximum amax:
+ *     alpha = amax / (6 * 448) for standard NVFP4, amax / (6 * 256) for Four Over Six,
+ *     because blocks scaled to 4 need a 1.5x larger E4M3 scale (Four Over Six explainer,
+ *     "Implementation details").
+ *   - rtn6 scales every block so its max maps to 6.  Four Over Six quantizes each block
+ *     twice, with its max mapped to 6 and to 4, measures both errors against the original
+ *     values, and keeps the smaller under the chosen rule: MSE, MAE or max error (Four
+ *     Over Six explainer, "Method / core mechanism", "Adaptive block scaling algorithm").
+ *     Ties keep 6.  A block scaled to 4 never uses FP4 values above 4.
+ *   - Simulated quantization returns the dequantized values in bf16, as a QAD student
+ *     forward uses them (Nemotron 3.5 Lightning NVFP4 news page, "two-stage QAD").
+ *
+ * Arithmetic: IEEE binary32 round-to-nearest-even steps, fixed order; the outputs are
+ * bit-identical to the CPU oracle that ships with the tests.  In short, per tensor
+ * alpha = RN(amax / C); per block, for each candidate Q: s = E4M3(RN(bmax / RN(Q*alpha)))
+ * (RNE, saturating at 448), d = RN(dec(s) * alpha), v_i = RN(x_i * RN(1/d)) (RN(x_i / d)
+ * when 1/d overflows), code_i = min(E2M1_RNE(|v_i|), Q), xhat_i = RN(val(code_i) * d),
+ * error accumulated over i = 0..15 in order (fma for MSE).
+ *
+ * Layouts (all row-major, blocks run along the last, contiguous dimension):
+ *   in        [E][rows][cols]     bf16 bit patterns (uint16), cols % 16 == 0
+ *   codes     [E][rows][cols/2]   uint8: element 2j in bits 0-3, element 2j+1 in bits 4-7;
+ *                                 code = sign << 3 | magnitude (E2M1: e1 e0 m, bias 1)
+ *   scales    [E][rows][cols/16]  uint8 E4M3FN (bias 7; 0x7E = 448; no swizzle)
+ *   alpha     [E]                 float32
+ *   out       [E][rows][cols]     bf16 (fake-quant)
+ * E = 1 for the non-batched calls.
+ *
+ * Ownership and ordering: every pointer is a device pointer owned by the caller.  The
+ * library allocates nothing and keeps no state; calls are reentrant.  All work is
+ * enqueued on `stream` (0 = the null stream) and the call returns at once; outputs are
+ * defined once the stream passes the call.  During a dynamic-scale call out_alpha holds
+ * the running amax, so it must not alias any other argument.  Fake-quant may run in
+ * place (out == in); any other overlap between arguments is rejected.
+ *
+ * Errors: argument errors are returned before anything is enqueued and leave the outputs
+ * untouched.  NVFP4_ERR_HIP reports a failed kernel launch.  Device faults surface at the
+ * caller's next synchronization.  Non-finite input is not an error: it poisons that
+ * tensor's outputs (alpha = NaN 0x7FC00000, every scale 0x7F, every code byte 0x00,
+ * every fake-quant value 0x7FC0).
+ */
+#ifndef NVFP4_AMAX_H
+#define NVFP4_AMAX_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+#define NVFP4_BLOCK 16
+
+typedef enum { NVFP4_RTN6 = 0, NVFP4_FOUR_OVER_SIX = 1 } nvfp4_mode;
+
+/* Four Over Six selection rule (ignored by rtn6 but still validated). */
+typedef enum { NVFP4_RULE_MSE = 0, NVFP4_RULE_MAE = 1, NVFP4_RULE_MAXERR = 2 } nvfp4_rule;
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,   /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,  /* E, rows or cols <= 0, cols % 16 != 0, E > 65535, size overflow */
+  NVFP4_ERR_BLOCK = 3,  /* block != 16 */
+  NVFP4_ERR_ENUM = 4,   /* mode or rule out of range */
+  NVFP4_ERR_ALIGN = 5,  /* in/out/codes not 16-byte aligned, alpha/amax not 4-byte */
+  NVFP4_ERR_ALIAS = 6,  /* overlapping arguments (other than in-place fake-quant) */
+  NVFP4_ERR_HIP = 7     /* a kernel launch failed */
+} nvfp4_status;
+
+/* ABI version (NVFP4_ABI_VERSION) and a static description of a status code. */
+int nvfp4_abi_version(void);
+const char* nvfp4_status_str(nvfp4_status status);
+
+/* Tensor amax: out_amax[e] = max |x| over tensor e of [E][rows][cols], exact (a max of
+ * bf16 magnitudes); +Inf or NaN when the tensor holds one (NaN wins).  The reduction
+ * that alpha is computed from (Four Over Six explainer, "Implementation details").
+ * Launches: a clear of out_amax, then one streaming pass. */
+nvfp4_status nvfp4_amax(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
+                        float* out_amax, hipStream_t stream);
+
+/* Packed NVFP4 quantization with a dynamic per-tensor scale: amax pass, then the block
+ * pass (both candidates and the selection in registers), then alpha is written.
+ * out_codes [rows][cols/2], out_scales [rows][cols/16], out_alpha [1]. */
+nvfp4_status nvfp4_quantize(const uint16_t* in, int64_t rows, int64_t cols, int block,
+                            nvfp4_mode mode, nvfp4_rule rule, uint8_t* out_codes,
+                            uint8_t* out_scales, float* out_alpha, hipStream_t stream);
+
+/* Simulated quantization: out = bf16(dequantize(quantize(in))), bit-identical to decoding
+ * the packed result of nvfp4_quantize.  out may equal in. */
+nvfp4_status nvfp4_fakequant(const uint16_t* in, int64_t rows, int64_t cols, int block,
+                             nvfp4_mode mode, nvfp4_rule rule, uint16_t* out,
+                             float* out_alpha, hipStream_t stream);
+
+/* E independent tensors [E][rows][cols] in one launch per pass, one alpha per tensor
+ * (e.g. the experts of a mixture-of-experts layer). */
+nvfp4_status nvfp4_quantize_batched(const uint16_t* in, int64_t E, int64_t rows,
+                                    int64_t cols, int block, nvfp4_mode mode,
+                                    nvfp4_rule rule, uint8_t* out_codes,
+                                    uint8_t* out_scales, float* out_alpha,
+                                    hipStream_t stream);
+nvfp4_status nvfp4_fakequant_batched(const uint16_t* in, int64_t E, int64_t rows,
+                                     int64_t cols, int block, nvfp4_mode mode,
+                                     nvfp4_rule rule, uint16_t* out, float* out_alpha,
+                                     hipStream_t stream);
+
+/* Fixed (static) scale: the caller supplies amax[E] (device memory, e.g. from a
+ * calibration or from nvfp4_amax) and the amax pass is skipped; alpha is derived from it
+ * exactly as in the dynamic calls (the Nemotron 3.5 Lightning NVFP4 news page offers
+ * dynamic and fixed scale settings, "workflow" paragraph).  Values beyond the supplied
+ * amax saturate: block scales clamp at 448, FP4 values at 6 (4 for blocks scaled to 4).
+ * nvfp4_amax followed by these calls is bit-identical to the dynamic calls.
+ * A non-finite amax poisons the tensor's outputs. */
+nvfp4_status nvfp4_quantize_from_amax(const uint16_t* in, int64_t E, int64_t rows,
+                                      int64_t cols, int block, nvfp4_mode mode,
+                                      nvfp4_rule rule, const float* amax,
+                                      uint8_t* out_codes, uint8_t* out_scales,
+                                      float* out_alpha, hipStream_t stream);
+nvfp4_status nvfp4_fakequant_from_amax(const uint16_t* in, int64_t E, int64_t rows,
+                                       int64_t cols, int block, nvfp4_mode mode,
+                                       nvfp4_rule rule, const float* amax, uint16_t* out,
+                                       float* out_alpha, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_AMAX_H */

@@ -1,0 +1,182 @@
+"""NVFP4 block-scaled quantization (rtn6 and Four Over Six) on MI355X.
+
+A thin ctypes binding over ``libnvfp4_amax.so`` (see ``include/nvfp4_amax.h``
+for the operation, layouts and errors).  This module only marshals arguments:
+torch provides device memory and the current stream; every step of the
+computation runs in the library's HIP kernels.  If the library is not built,
+every call raises -- there is no fallback.
+
+    codes, scales, alpha = quantize(x, "four_over_six", "mse")
+    y, alpha = fakequant(x, "four_over_six", "mae")
+
+x is a contiguous bf16 CUDA tensor [rows, cols] or [E, rows, cols] (a leading
+expert dimension selects the batched entry points), cols % 16 == 0.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["quantize", "fakequant", "amax", "quantize_from_amax", "fakequant_from_amax",
+           "lib", "NVFP4Error", "MODES", "RULES", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_amax.so")
+MODES = {"rtn6": 0, "four_over_six": 1}
+RULES = {"mse": 0, "mae": 1, "maxerr": 2}
+BLOCK = 16
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib().nvfp4_status_str(status).decode()
+        super().__init__("%s: %s (status %d)" % (where, msg, status))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The C ABI with argument types set.  Raises if the HIP library is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libnvfp4_amax.so is not built (run __graft_entry__.build() or "
+                               "python -m nvfp4_block_scaled_amax_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.nvfp4_abi_version.restype = i32
+        L.nvfp4_status_str.argtypes, L.nvfp4_status_str.restype = [i32], ctypes.c_char_p
+        L.nvfp4_amax.argtypes = [P, i64, i64, i64, P, P]
+        L.nvfp4_quantize.argtypes = [P, i64, i64, i32, i32, i32, P, P, P, P]
+        L.nvfp4_fakequant.argtypes = [P, i64, i64, i32, i32, i32, P, P, P]
+        L.nvfp4_quantize_batched.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
+        L.nvfp4_fakequant_batched.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P]
+        L.nvfp4_quantize_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P]
+        L.nvfp4_fakequant_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
+        for name in ("nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
+                     "nvfp4_fakequant_batched", "nvfp4_quantize_from_amax",
+                     "nvfp4_fakequant_from_amax"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise NVFP4Error(status, where)
+
+
+def _mode(m) -> int:
+    return MODES[m] if isinstance(m, str) else int(m)
+
+
+def _rule(r) -> int:
+    return RULES[r] if isinstance(r, str) else int(r)
+
+
+def _dims(x: torch.Tensor):
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16, got %s" % x.dtype)
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if x.dim() == 2:
+        return 1, x.shape[0], x.shape[1], False
+    if x.dim() == 3:
+        return x.shape[0], x.shape[1], x.shape[2], True
+    raise ValueError("x must be [rows, cols] or [E, rows, cols]")
+
+
+def _stream(x: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _out(t, shape, dtype, like):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() \
+            or t.device != like.device:
+        raise ValueError("output must be a contiguous %s tensor of shape %s on %s"
+                         % (dtype, tuple(shape), like.device))
+    return t
+
+
+def amax(x: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """Per-tensor max |x| (float32 [E], E = 1 for a 2-D x)."""
+    E, rows, cols, _ = _dims(x)
+    out = _out(out, (E,), torch.float32, x)
+    _check(lib().nvfp4_amax(_ptr(x), E, rows, cols, _ptr(out), _stream(x)), "nvfp4_amax")
+    return out
+
+
+def _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha):
+    lead = (E,) if batched else ()
+    codes = _out(codes, lead + (rows, cols // 2), torch.uint8, x)
+    scales = _out(scales, lead + (rows, cols // 16), torch.uint8, x)
+    alpha = _out(alpha, (E,), torch.float32, x)
+    return codes, scales, alpha
+
+
+def quantize(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=None, scales=None,
+             alpha=None):
+    """Packed NVFP4 with a dynamic per-tensor scale -> (codes, scales, alpha)."""
+    E, rows, cols, batched = _dims(x)
+    codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha)
+    if batched:
+        st = lib().nvfp4_quantize_batched(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                          _ptr(codes), _ptr(scales), _ptr(alpha), _stream(x))
+    else:
+        st = lib().nvfp4_quantize(_ptr(x), rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                  _ptr(codes), _ptr(scales), _ptr(alpha), _stream(x))
+    _check(st, "nvfp4_quantize")
+    return codes, scales, alpha
+
+
+def fakequant(x: torch.Tensor, mode="four_over_six", rule="mse", *, out=None, alpha=None):
+    """bf16 quantize-dequantize with a dynamic per-tensor scale -> (y, alpha).
+    out may be x itself (in place)."""
+    E, rows, cols, batched = _dims(x)
+    out = _out(out, x.shape, torch.bfloat16, x)
+    alpha = _out(alpha, (E,), torch.float32, x)
+    if batched:
+        st = lib().nvfp4_fakequant_batched(_ptr(x), E, rows, cols, BLOCK, _mode(mode),
+                                           _rule(rule), _ptr(out), _ptr(alpha), _stream(x))
+    else:
+        st = lib().nvfp4_fakequant(_ptr(x), rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                   _ptr(out), _ptr(alpha), _stream(x))
+    _check(st, "nvfp4_fakequant")
+    return out, alpha
+
+
+def quantize_from_amax(x: torch.Tensor, amax_: torch.Tensor, mode="four_over_six", rule="mse",
+                       *, codes=None, scales=None, alpha=None):
+    """Packed NVFP4 with a caller-supplied amax (float32 [E] on the GPU)."""
+    E, rows, cols, batched = _dims(x)
+    amax_ = _out(amax_, (E,), torch.float32, x)
+    codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha)
+    st = lib().nvfp4_quantize_from_amax(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                        _ptr(amax_), _ptr(codes), _ptr(scales), _ptr(alpha),
+                                        _stream(x))
+    _check(st, "nvfp4_quantize_from_amax")
+    return codes, scales, alpha
+
+
+def fakequant_from_amax(x: torch.Tensor, amax_: torch.Tensor, mode="four_over_six", rule="mse",
+                        *, out=None, alpha=None):
+    """bf16 quantize-dequantize with a caller-supplied amax."""
+    E, rows, cols, batched = _dims(x)
+    amax_ = _out(amax_, (E,), torch.float32, x)
+    out = _out(out, x.shape, torch.bfloat16, x)
+    alpha = _out(alpha, (E,), torch.float32, x)
+    st = lib().nvfp4_fakequant_from_amax(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                         _ptr(amax_), _ptr(out), _ptr(alpha), _stream(x))
+    _check(st, "nvfp4_fakequant_from_amax")
+    return out, alpha

@@ -1,0 +1,323 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, bit for bit.
+
+Codes, scale bytes, alpha bits and fake-quant bf16 bits must be identical (the
+arithmetic is binary32 round-to-nearest-even in a fixed order on both sides, so
+the bar is exact equality).  Small tensors are compared whole; the five full-size
+workloads run in the launch configuration the benchmark times and are compared on
+sampled blocks, plus a property that holds at any size (decoding the packed
+output gives the fake-quant output)."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import bf16_bits, bf16_to_f32
+from nvfp4_block_scaled_amax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = max(1, min(16, os.cpu_count() or 1))
+RUNS = [("rtn6", "mse"), ("four_over_six", "mse"), ("four_over_six", "mae"),
+        ("four_over_six", "maxerr")]
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def nv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_block_scaled_amax_amd as m
+    m.lib()          # raises if the HIP library is missing: no fallback
+    return m
+
+
+def to_gpu(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).cuda()
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def gpu_run(nv, xg, mode, rule, fq):
+    if fq:
+        y, al = nv.fakequant(xg, mode, rule)
+        torch.cuda.synchronize()
+        return dict(y=u16(y), alpha=al.cpu().numpy())
+    c, s, al = nv.quantize(xg, mode, rule)
+    torch.cuda.synchronize()
+    return dict(codes=c.cpu().numpy(), scales=s.cpu().numpy(), alpha=al.cpu().numpy())
+
+
+def assert_same(got, ref, fq, tag):
+    assert np.array_equal(got["alpha"].view(np.uint32),
+                          np.asarray(ref["alpha"], np.float32).view(np.uint32)), tag
+    if fq:
+        bad = np.nonzero(got["y"].ravel() != ref["y"].ravel())[0]
+        assert bad.size == 0, "%s: %d fake-quant mismatches, first at %s" % (tag, bad.size, bad[:4])
+    else:
+        bs = np.nonzero(got["scales"].ravel() != ref["scales"].ravel())[0]
+        assert bs.size == 0, "%s: %d scale mismatches, first blocks %s" % (tag, bs.size, bs[:4])
+        bc = np.nonzero(got["codes"].ravel() != ref["codes"].ravel())[0]
+        assert bc.size == 0, "%s: %d code-byte mismatches, first at %s" % (tag, bc.size, bc[:4])
+
+
+def check_full(nv, orc, xbits, mode, rule, fq, tag):
+    say("[parity] %s shape=%s mode=%s rule=%s fq=%s" % (tag, xbits.shape, mode, rule, fq))
+    got = gpu_run(nv, to_gpu(xbits), mode, rule, fq)
+    ref = orc.quantize(xbits, mode, rule, nthreads=NTHREADS, want_y=fq)
+    assert_same(got, ref, fq, tag)
+
+
+# ----------------------------------------------------------------------------- small, whole
+def test_tiny_workload_both_runs(nv, orc):
+    x = W.bits(W.generate("tiny"))
+    for mode, rule in (("rtn6", "mse"), ("four_over_six", "mse")):
+        for fq in (False, True):
+            check_full(nv, orc, x, mode, rule, fq, "tiny")
+
+
+SMALL = [("tiny", (300, 272)), ("weight", (200, 1792)), ("act", (301, 1024)),
+         ("large", (97, 3584)), ("moe", (5, 130, 320))]
+
+
+@pytest.mark.parametrize("name,shape", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
+@pytest.mark.parametrize("fq", [False, True], ids=["packed", "fakequant"])
+def test_small_workloads_whole(nv, orc, name, shape, mode, rule, fq):
+    """Several workgroups per tensor and a ragged last workgroup."""
+    check_full(nv, orc, W.bits(W.generate(name, shape)), mode, rule, fq, name)
+
+
+def test_random_shapes(nv, orc):
+    rng = np.random.default_rng(77)
+    for k in range(24):
+        rows = int(rng.integers(1, 34))
+        cols = int(rng.integers(1, 257)) * 16
+        E = int(rng.integers(1, 4)) if k % 3 == 0 else None
+        shape = (E, rows, cols) if E else (rows, cols)
+        x = W.bits(W.normal(shape, seed=1000 + k, sigma=float(np.exp(rng.uniform(-8, 8)))))
+        mode, rule = RUNS[k % 4]
+        check_full(nv, orc, x, mode, rule, bool(k % 2), "random%d" % k)
+
+
+# ----------------------------------------------------------------------------- edge cases
+def _edge_tensors():
+    rng = np.random.default_rng(5)
+    out = {}
+    z = np.zeros((4, 64), np.uint16)
+    z[1, 3] = 0x8000
+    z[2, :] = 0x8000
+    out["zeros"] = z
+    # every bf16 magnitude from subnormal up, so alpha is a binary32 subnormal and the
+    # E4M3 clamp and the 1/d-overflow division path are live
+    out["subnormal"] = (rng.integers(0, 0x0180, size=(8, 128), dtype=np.uint16) |
+                        (rng.integers(0, 2, size=(8, 128), dtype=np.uint16) << 15))
+    out["tiny_normal"] = (rng.integers(0x0080, 0x0800, size=(8, 128), dtype=np.uint16) |
+                          (rng.integers(0, 2, size=(8, 128), dtype=np.uint16) << 15))
+    big = rng.integers(0x7E00, 0x7F80, size=(6, 96), dtype=np.uint16)
+    big[0, 0] = 0x7F7F                                   # the largest finite bf16
+    out["huge"] = big | (rng.integers(0, 2, size=big.shape, dtype=np.uint16) << 15)
+    # dense exact ties: many blocks whose values sit on FP4 midpoints
+    t = bf16_bits(np.tile(np.array([6, 5, 3.5, 2.5, 1.75, 1.25, .75, .25, -5, -3.5, -2.5,
+                                    -1.75, -1.25, -.75, -.25, 0], np.float32), (16, 4)))
+    out["ties"] = t
+    # blocks far below the tensor amax (scale byte 0 and subnormal scales)
+    w = W.bits(W.normal((16, 256), seed=9, sigma=1e-4))
+    w[0, 0] = bf16_bits([28672.0])[0]
+    out["dynamic_range"] = w
+    out["one_row_one_block"] = W.bits(W.normal((1, 16), seed=10))
+    out["one_column_of_blocks"] = W.bits(W.normal((37, 16), seed=11))
+    return out
+
+
+EDGE = _edge_tensors()
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+@pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
+def test_edge_cases(nv, orc, name, mode, rule):
+    for fq in (False, True):
+        check_full(nv, orc, EDGE[name], mode, rule, fq, name)
+
+
+@pytest.mark.parametrize("bad", [0x7FC0, 0x7F80, 0xFF80, 0xFFC1])
+def test_non_finite_poisons_only_its_tensor(nv, orc, bad):
+    x = W.bits(W.generate("moe", (3, 16, 64))).copy()
+    x[1, 5, 17] = bad
+    for mode, rule in (("rtn6", "mse"), ("four_over_six", "mae")):
+        for fq in (False, True):
+            check_full(nv, orc, x, mode, rule, fq, "poison")
+    am = nv.amax(to_gpu(x))
+    torch.cuda.synchronize()
+    a = am.cpu().numpy()
+    assert not np.isfinite(a[1]) and np.isfinite(a[0]) and np.isfinite(a[2])
+
+
+# ----------------------------------------------------------------------------- amax, fixed scale
+def test_amax_matches_oracle(nv, orc):
+    for name, shape in SMALL:
+        x = W.bits(W.generate(name, shape))
+        E = x.shape[0] if x.ndim == 3 else 1
+        got = nv.amax(to_gpu(x)).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), orc.amax(x, E).view(np.uint32)), name
+
+
+@pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
+def test_fixed_scale_entry(nv, orc, mode, rule):
+    x = W.bits(W.generate("moe", (3, 40, 160)))
+    xg = to_gpu(x)
+    # 1. amax pass + fixed-scale pass == the dynamic call
+    am = nv.amax(xg)
+    c1, s1, a1 = nv.quantize_from_amax(xg, am, mode, rule)
+    c2, s2, a2 = nv.quantize(xg, mode, rule)
+    y1, b1 = nv.fakequant_from_amax(xg, am, mode, rule)
+    y2, b2 = nv.fakequant(xg, mode, rule)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2) and torch.equal(y1, y2)
+    assert torch.equal(a1, a2) and torch.equal(b1, b2)
+    # 2. a static amax below the true one: scales clamp at 448 and values saturate
+    true_amax = orc.amax(x, 3)
+    static = (true_amax * np.float32(0.3)).astype(np.float32)
+    static[1] = -static[1]                                   # the magnitude is used
+    sg = torch.from_numpy(static).cuda()
+    c, s, a = nv.quantize_from_amax(xg, sg, mode, rule)
+    y, _ = nv.fakequant_from_amax(xg, sg, mode, rule)
+    torch.cuda.synchronize()
+    al = np.array([orc.alpha(abs(float(v)), mode) for v in static], np.float32)
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), al.view(np.uint32))
+    ids = np.arange(x.size // 16)
+    ref = orc.quantize_blocks(x, al, ids, mode, rule)
+    assert np.array_equal(c.cpu().numpy().reshape(-1, 8), ref["codes"])
+    assert np.array_equal(s.cpu().numpy().ravel(), ref["scales"])
+    assert np.array_equal(u16(y).reshape(-1, 16), ref["y"])
+    if mode == "rtn6":
+        assert (ref["scales"] == 0x7E).any()                  # the clamp was exercised
+
+
+# ----------------------------------------------------------------------------- in place, guards
+def test_in_place_fakequant(nv, orc):
+    x = W.bits(W.generate("act", (64, 512)))
+    xg = to_gpu(x)
+    y, al = nv.fakequant(xg, "four_over_six", "mae", out=xg)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == xg.data_ptr()
+    ref = orc.quantize(x, "four_over_six", "mae")
+    assert np.array_equal(u16(xg), ref["y"])
+
+
+def test_no_writes_outside_outputs(nv, orc):
+    """Outputs live inside larger buffers filled with a canary; only the output bytes may
+    change."""
+    x = W.bits(W.generate("large", (33, 240)))           # 495 blocks: ragged
+    xg = to_gpu(x)
+    G = 4096
+    nb = x.size // 16
+    for fq in (False, True):
+        if fq:
+            buf = torch.full((G + x.size + G,), 0x5A5A, dtype=torch.int32, device="cuda") \
+                .to(torch.int16)
+            out = buf[G:G + x.size].view(torch.bfloat16).view(x.shape)
+            abuf = torch.full((64 + 1 + 64,), 7.5, dtype=torch.float32, device="cuda")
+            nv.fakequant(xg, "four_over_six", "mse", out=out, alpha=abuf[64:65])
+            torch.cuda.synchronize()
+            hb = buf.cpu().numpy()
+            assert (hb[:G] == 0x5A5A).all() and (hb[G + x.size:] == 0x5A5A).all()
+        else:
+            cbuf = torch.full((G + nb * 8 + G,), 0xA5, dtype=torch.uint8, device="cuda")
+            sbuf = torch.full((G + nb + 3 + G,), 0xA5, dtype=torch.uint8, device="cuda")
+            abuf = torch.full((64 + 1 + 64,), 7.5, dtype=torch.float32, device="cuda")
+            codes = cbuf[G:G + nb * 8].view(x.shape[0], x.shape[1] // 2)
+            scales = sbuf[G + 3:G + 3 + nb].view(x.shape[0], x.shape[1] // 16)
+            nv.quantize(xg, "four_over_six", "mse", codes=codes, scales=scales,
+                        alpha=abuf[64:65])
+            torch.cuda.synchronize()
+            hc, hs = cbuf.cpu().numpy(), sbuf.cpu().numpy()
+            assert (hc[:G] == 0xA5).all() and (hc[G + nb * 8:] == 0xA5).all()
+            assert (hs[:G + 3] == 0xA5).all() and (hs[G + 3 + nb:] == 0xA5).all()
+        ha = abuf.cpu().numpy()
+        assert (ha[:64] == 7.5).all() and (ha[65:] == 7.5).all()
+
+
+# ----------------------------------------------------------------------------- full size
+_FULL = {}
+
+
+def full_input(name):
+    if name not in _FULL:
+        _FULL.clear()
+        say("[full] generating %s %s" % (name, W.WORKLOADS[name].shape))
+        _FULL[name] = W.generate(name)
+    return _FULL[name]
+
+
+FULL_CASES = [(w.name, mode, rule, out == "fakequant") for w in W.WORKLOADS.values()
+              for (mode, rule, out) in w.runs]
+
+
+def _decode_packed(codes, scales, alpha, shape):
+    """Packed NVFP4 -> bf16 with torch ops on the GPU (IEEE binary32 multiplies and the
+    round-to-nearest-even bf16 cast): val(code) * RN(dec(scale) * alpha)."""
+    fp4 = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6, -0.0, -.5, -1, -1.5, -2, -3, -4, -6],
+                       dtype=torch.float32, device=codes.device)
+    c = codes.reshape(-1, 8).to(torch.int32)
+    nib = torch.stack([c & 15, c >> 4], dim=-1).reshape(-1, 16)
+    dec = scales.reshape(-1).view(torch.float8_e4m3fn).to(torch.float32)
+    E = alpha.numel()
+    step = dec.view(E, -1) * alpha.view(E, 1)
+    xhat = fp4[nib.long()] * step.reshape(-1, 1)
+    return xhat.to(torch.bfloat16).view(shape)
+
+
+@pytest.mark.parametrize("name,mode,rule,fq", FULL_CASES,
+                         ids=["%s-%s-%s" % (c[0], c[1], c[2]) for c in FULL_CASES])
+def test_full_size_workloads_sampled(nv, orc, name, mode, rule, fq):
+    xt = full_input(name)
+    x = W.bits(xt)
+    E = x.shape[0] if x.ndim == 3 else 1
+    say("[full] %s %s/%s fq=%s" % (name, mode, rule, fq))
+    xg = xt.cuda()
+    nb = x.size // 16
+    amax = orc.amax(x, E)
+    al = np.array([orc.alpha(float(a), mode) for a in amax], np.float32)
+    rng = np.random.default_rng(123)
+    per = nb // E
+    ids = np.unique(np.concatenate(
+        [rng.integers(0, nb, size=20000)] +
+        [np.arange(e * per, e * per + 256) for e in range(E)] +
+        [np.arange((e + 1) * per - 256, (e + 1) * per) for e in range(E)]))
+    ref = orc.quantize_blocks(x, al, ids, mode, rule)
+    if fq:
+        y, a = nv.fakequant(xg, mode, rule)
+        torch.cuda.synchronize()
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), al.view(np.uint32))
+        yb = u16(y).reshape(-1, 16)
+        assert np.array_equal(yb[ids], ref["y"])
+        # at full size: the packed result decodes to this fake-quant output
+        c, s, a2 = nv.quantize(xg, mode, rule)
+        dq = _decode_packed(c, s, a2, xg.shape)
+        torch.cuda.synchronize()
+        assert torch.equal(dq.view(torch.int16), y.view(torch.int16))
+    else:
+        c, s, a = nv.quantize(xg, mode, rule)
+        torch.cuda.synchronize()
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), al.view(np.uint32))
+        cb = c.cpu().numpy().reshape(-1, 8)
+        sb = s.cpu().numpy().reshape(-1)
+        assert np.array_equal(cb[ids], ref["codes"])
+        assert np.array_equal(sb[ids], ref["scales"])
+        if name in ("tiny", "weight"):                        # small enough to decode whole
+            y, _ = nv.fakequant(xg, mode, rule)
+            dq = _decode_packed(c, s, a, xg.shape)
+            torch.cuda.synchronize()
+            assert torch.equal(dq.view(torch.int16), y.view(torch.int16))
+    del xg
+    torch.cuda.empty_cache()
