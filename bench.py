@@ -172,7 +172,16 @@ def main():
                   "GBps": round(pass_gbps, 1), "frac_hbm": round(pass_gbps / HBM_PEAK_GBPS, 4)},
     }
 
-    if not args.profile:
+    if args.profile:
+        # a plain device copy of known size (256 MiB read + 256 MiB written), so that a
+        # counter run of this command can calibrate FETCH_SIZE / WRITE_SIZE against it
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    else:
         # ---- block pass alone on cold buffers (no amax pass before it), and rtn6 on the same
         def time_pass(mode, rule, reps):
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
@@ -241,6 +250,8 @@ def cpu_baseline(x_cpu, wl, args, step_bpe):
     """The CPU oracle (untuned, test infrastructure) on a bounded sample of the workload:
     the leading rows of the tensor (of the first experts for batched workloads), the whole
     hot path (amax + block pass), on the host's cores."""
+    import numpy as np
+
     import oracle
     from nvfp4_block_scaled_amax_amd import workloads as W
     cores = max(1, min(16, os.cpu_count() or 1))
@@ -253,11 +264,16 @@ def cpu_baseline(x_cpu, wl, args, step_bpe):
         sample = x[:rows]
         desc = "first %d of %d rows (%d elements)" % (rows, x.shape[0], sample.size)
     oracle.build()
-    t0 = time.perf_counter()
-    oracle.quantize(sample, args.mode, args.rule, nthreads=cores, want_y=False)
-    dt = time.perf_counter() - t0
+    reps, times = 0, []
+    while reps < 20 and (reps < 3 or sum(times) < 10.0):     # about 10 s of wall clock
+        t0 = time.perf_counter()
+        oracle.quantize(sample, args.mode, args.rule, nthreads=cores, want_y=False)
+        times.append(time.perf_counter() - t0)
+        reps += 1
+    dt = float(np.median(times))
     return {"value": round(step_bpe * sample.size / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle", "sample": desc, "seconds": round(dt, 2)}
+            "kind": "oracle", "sample": desc + ", median of %d runs" % reps,
+            "seconds_per_run": round(dt, 3)}
 
 
 if __name__ == "__main__":

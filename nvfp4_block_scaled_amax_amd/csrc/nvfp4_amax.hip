@@ -70,12 +70,6 @@ __device__ __forceinline__ float e2m1_value_of(uint32_t m) {
   return m < 2 ? 0.5f * (float)m : __uint_as_float((m + 252u) << 22);
 }
 
-// binary32 (finite) -> bfloat16 bits, round to nearest even.
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // ----------------------------------------------------------------------------- kernels
 __global__ void clear_kernel(uint32_t* __restrict__ acc, int64_t E) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -111,32 +105,36 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-// Grid: x = workgroups per tensor, y = tensor.  Each workgroup strides over the tensor's
-// 16-byte chunks (8 bf16 values), four loads in flight per lane.
-__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ in,
-                                                        int64_t chunks, uint32_t* __restrict__ acc) {
+// Grid: x = workgroups per tensor, y = tensor.  Few, large workgroups (one atomic each:
+// same-address atomics serialize, so their count is kept near the CU count), each
+// striding over the tensor's 16-byte chunks (8 bf16 values) with 8 loads in flight.
+constexpr int kAmaxThreads = 1024;
+constexpr int kAmaxWGs = 256;
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restrict__ in,
+                                                            int64_t chunks,
+                                                            uint32_t* __restrict__ acc) {
+  constexpr int U = 8;
   const uint4* p = in + (int64_t)blockIdx.y * chunks;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
   uint32_t m = 0;
-  for (; i + 3 * stride < chunks; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    m = mag_max8(m, a);
-    m = mag_max8(m, b);
-    m = mag_max8(m, c);
-    m = mag_max8(m, d);
+  for (; i + (U - 1) * stride < chunks; i += U * stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = p[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < U; ++k) m = mag_max8(m, v[k]);
   }
   for (; i < chunks; i += stride) m = mag_max8(m, p[i]);
   // the larger of the two 16-bit magnitudes, as the bits of a binary32 value
   m = max(m & 0xFFFFu, m >> 16) << 16;
   m = wave_max_u32(m);
-  __shared__ uint32_t part[kThreads / 64];
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) part[wave] = m;
+  __shared__ uint32_t part[kAmaxThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = part[0];
-    for (int w = 1; w < kThreads / 64; ++w) r = max(r, part[w]);
+    for (int w = 1; w < kAmaxThreads / 64; ++w) r = max(r, part[w]);
     atomicMax(acc + blockIdx.y, r);
   }
 }
@@ -149,108 +147,347 @@ __global__ void alpha_kernel(const uint32_t* amax_bits, float* alpha,
   alpha[i] = a >= 0x7F800000u ? __uint_as_float(0x7FC00000u) : __uint_as_float(a) / C;
 }
 
-// One candidate block maximum (Q = 6, or 4 under Four Over Six), all in registers.
-// Returns the error under RULE; writes the scale byte, the 16 codes as two packed words
-// and (FQ) the 16 dequantized values.
-template <int RULE, bool FQ>
-__device__ __forceinline__ float run_candidate(const float (&x)[16], float bmax, float alpha,
-                                               float cq, uint32_t cap, uint32_t& scale,
-                                               uint32_t& w0, uint32_t& w1, float (&xh)[16]) {
+// ----------------------------------------------------------------------------- block pass
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+#ifndef NVFP4_UNIT_BLOCKS
+#define NVFP4_UNIT_BLOCKS 1          // 16-element blocks owned by one lane per step
+#endif
+#ifndef NVFP4_PREFETCH
+#define NVFP4_PREFETCH 1             // grid-stride steps whose loads are in flight ahead
+#endif
+#ifndef NVFP4_SPLIT_CANDIDATES
+#define NVFP4_SPLIT_CANDIDATES 0
+#endif
+#ifndef NVFP4_WAVES_PER_EU
+#define NVFP4_WAVES_PER_EU 4         // occupancy floor: caps the block pass at 128 VGPRs
+#endif
+#ifndef NVFP4_BLOCK_WGS
+#define NVFP4_BLOCK_WGS 1024         // target workgroups of the block pass (all tensors)
+#endif
+
+// Reference path for one candidate, straight from the definition, one binary32 step at a
+// time (correctly rounded division and reciprocal, threshold-count FP4 rounding).  The
+// table-driven path below covers every block except three rare kinds, which come here:
+// a block max below 2^-126, a tensor alpha below 2^-118, and a block scaled to 4 whose
+// scaled values may pass 5 (so that the cap at FP4 value 4 bites).  The loop is kept
+// rolled and re-reads the block's values (cache-resident) so that this path adds almost
+// no registers to the kernel: the hot loop's occupancy is set by the fast path alone.
+template <int RULE>
+__device__ __forceinline__ float ref_candidate(const uint16_t* __restrict__ xb, float bmax,
+                                               float alpha, float cq, uint32_t cap,
+                                               uint32_t& scale, float& d_out, uint32_t& w0,
+                                               uint32_t& w1) {
   const float sigma = alpha == 0.0f ? 0.0f : bmax / cq;
   scale = e4m3_from_f32(sigma);
   const float d = e4m3_to_f32(scale) * alpha;
+  d_out = d;
   const float r = d == 0.0f ? 0.0f : 1.0f / d;
-  const bool r_finite = r != __builtin_inff();
-  float v[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = x[i] * r;
-  if (!r_finite) {                 // 1/d overflows: only when alpha is a binary32 subnormal
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = x[i] / d;
-  }
+  const bool r_finite = r != __builtin_inff();   // 1/d overflows only for tiny alpha
   float acc = 0.0f;
-  w0 = 0u;
-  w1 = 0u;
-#pragma unroll
+  uint32_t lo = 0u, hi = 0u;
+#pragma unroll 1
   for (int i = 0; i < 16; ++i) {
-    const uint32_t m = min(e2m1_code_of(fabsf(v[i])), cap);
-    const uint32_t sgn = __float_as_uint(x[i]) & 0x80000000u;
+    const float x = __uint_as_float((uint32_t)xb[i] << 16);
+    const float v = r_finite ? x * r : x / d;
+    const uint32_t m = min(e2m1_code_of(fabsf(v)), cap);
+    const uint32_t sgn = __float_as_uint(x) & 0x80000000u;
     const float xhat = __uint_as_float(__float_as_uint(e2m1_value_of(m) * d) | sgn);
-    const float e = x[i] - xhat;
+    const float e = x - xhat;
     if (RULE == NVFP4_RULE_MSE)      acc = __builtin_fmaf(e, e, acc);
     else if (RULE == NVFP4_RULE_MAE) acc = acc + fabsf(e);
     else                             acc = fmaxf(acc, fabsf(e));
-    const uint32_t code = (sgn >> 28) | m;
-    if (i < 8) w0 |= code << (4 * i);
-    else       w1 |= code << (4 * (i - 8));
-    if (FQ) xh[i] = xhat;
+    const uint32_t code = ((sgn >> 28) | m) << (4 * (i & 7));
+    if (i < 8) lo |= code;
+    else       hi |= code;
   }
+  w0 = lo;
+  w1 = hi;
   return acc;
 }
 
-// Grid: x = ceil(blocks per tensor / 256), y = tensor.  Lane = one 16-element block.
-template <int MODE, int RULE, bool FQ>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(
-    const uint4* __restrict__ in, int64_t nblk, const float* __restrict__ amax,
-    uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
-    float* __restrict__ alpha_out) {
-  const int64_t t = blockIdx.y;
-  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const uint32_t abits = __float_as_uint(amax[t]) & 0x7FFFFFFFu;
-  // alpha_out (distinct from amax) is written by the first lane of each tensor
-  if (alpha_out && b == 0)
-    alpha_out[t] = abits >= 0x7F800000u ? __uint_as_float(0x7FC00000u)
-                   : __uint_as_float(abits) / (MODE == NVFP4_FOUR_OVER_SIX ? kC6x256 : kC6x448);
-  if (b >= nblk) return;
-  const int64_t g = t * nblk + b;
-  if (abits >= 0x7F800000u) {      // non-finite input or amax: poison the tensor
-    if (FQ) {
-      const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-      out[2 * g] = nan4;
-      out[2 * g + 1] = nan4;
-    } else {
-      codes[g] = make_uint2(0u, 0u);
-      scales[g] = 0x7F;
-    }
-    return;
+struct RefOut {
+  uint32_t s, w0, w1;
+  float d;
+};
+
+// Returned by value (in registers): outputs passed by reference would make the caller
+// keep them in scratch memory on every step of the hot loop.
+template <int MODE, int RULE>
+__device__ __noinline__ RefOut ref_block(const uint16_t* __restrict__ xb, float bmax,
+                                         float alpha) {
+  RefOut o;
+  const float err6 = ref_candidate<RULE>(xb, bmax, alpha, 6.0f * alpha, 7u, o.s, o.d, o.w0, o.w1);
+  if (MODE == NVFP4_FOUR_OVER_SIX) {
+    uint32_t s4, a4, b4;
+    float d4;
+    const float err4 = ref_candidate<RULE>(xb, bmax, alpha, 4.0f * alpha, 6u, s4, d4, a4, b4);
+    if (err4 < err6) { o.s = s4; o.d = d4; o.w0 = a4; o.w1 = b4; }   // ties keep 6
   }
-  const float alpha = __uint_as_float(abits) / (MODE == NVFP4_FOUR_OVER_SIX ? kC6x256 : kC6x448);
-  const uint4 p0 = in[2 * g], p1 = in[2 * g + 1];
+  return o;
+}
+
+// max(acc, |a|, |b|) in one v_max3_f32.  fmaxf on values built from integer bits makes
+// the compiler canonicalize each operand first (three instructions per pair); no NaN
+// reaches this code (non-finite tensors are poisoned before), so the plain max is exact.
+__device__ __forceinline__ float max3_abs(float acc, float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(acc), "v"(a), "v"(b));
+  return r;
+}
+
+// One pair of elements of one candidate: v = x*r, FP4 round (hardware, round to nearest
+// even, saturating at 6, sign kept), decode, xhat = val*d, error into the running sum.
+// SEL (0..3) is the byte of the code word the pair lands in.
+template <int RULE, int SEL>
+__device__ __forceinline__ void fp4_pair(float xa, float xb, float r, float d, uint32_t& word,
+                                         float& acc) {
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, xa * r, xb * r, 1.0f, SEL);
+  const f32x2 val = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+  const float ea = xa - val.x * d;
+  const float eb = xb - val.y * d;
+  if (RULE == NVFP4_RULE_MSE) {
+    acc = __builtin_fmaf(ea, ea, acc);
+    acc = __builtin_fmaf(eb, eb, acc);
+  } else if (RULE == NVFP4_RULE_MAE) {
+    acc = acc + fabsf(ea);
+    acc = acc + fabsf(eb);
+  } else {
+    acc = fmaxf(acc, fmaxf(fabsf(ea), fabsf(eb)));
+  }
+}
+
+// One candidate, table-driven: 8 code bytes in two words, returns the error.
+template <int RULE>
+__device__ __forceinline__ float fast_candidate(const float (&x)[16], float r, float d,
+                                                uint32_t& w0, uint32_t& w1) {
+  float acc = 0.0f;
+  // all four bytes of each word are written below, so their start value is irrelevant
+  w0 = __float_as_uint(x[0]);
+  w1 = __float_as_uint(x[1]);
+  fp4_pair<RULE, 0>(x[0], x[1], r, d, w0, acc);
+  fp4_pair<RULE, 1>(x[2], x[3], r, d, w0, acc);
+  fp4_pair<RULE, 2>(x[4], x[5], r, d, w0, acc);
+  fp4_pair<RULE, 3>(x[6], x[7], r, d, w0, acc);
+  fp4_pair<RULE, 0>(x[8], x[9], r, d, w1, acc);
+  fp4_pair<RULE, 1>(x[10], x[11], r, d, w1, acc);
+  fp4_pair<RULE, 2>(x[12], x[13], r, d, w1, acc);
+  fp4_pair<RULE, 3>(x[14], x[15], r, d, w1, acc);
+  return acc;
+}
+
+// Per-tensor tables in LDS.
+//   D[s] = (d, r): the step d = RN(dec(s) * alpha) of E4M3 byte s and r = RN(1/d) (0 if d = 0)
+//   T[k] = (T6, T4): RN((1 + k/128) / m_Q) where Q*alpha = m_Q * 2^p_Q, m_Q in [0.5, 1).
+// A normal block max is bmax = (1 + k/128) * 2^(e-127) (bf16: 7 fraction bits), so
+// bmax / (Q*alpha) = ((1 + k/128) / m_Q) * 2^(e-127-p_Q), and because rounding to binary32
+// commutes with scaling by a power of two while the result stays normal,
+// RN(bmax / (Q*alpha)) = ldexp(T_Q[k], e-127-p_Q).  Results below 2^-126 become scale byte
+// 0 either way.  This replaces two divisions and two reciprocals per block.
+struct BlockTables {
+  f32x2 D[256];
+  f32x2 T[128];
+};
+
+template <int MODE>
+__device__ __forceinline__ void build_tables(BlockTables& tb, float alpha, int& n6, int& n4) {
+  const int i = threadIdx.x;
+  const float c6 = 6.0f * alpha, c4 = 4.0f * alpha;
+  int p6 = 0, p4 = 0;
+  const float m6 = frexpf(c6, &p6);
+  const float m4 = frexpf(c4, &p4);
+  n6 = 127 + p6;
+  n4 = 127 + p4;
+  if (i < 256) {
+    const float d = e4m3_to_f32((uint32_t)i & 0x7Fu) * alpha;
+    tb.D[i] = f32x2{d, d == 0.0f ? 0.0f : 1.0f / d};
+  }
+  if (i < 128) {
+    const float mk = 1.0f + (float)i * 0.0078125f;
+    tb.T[i] = f32x2{mk / m6, MODE == NVFP4_FOUR_OVER_SIX ? mk / m4 : 0.0f};
+  }
+}
+
+// Whole block: bmax, both candidate scales from the tables, both trials, selection.
+// Writes the chosen scale byte s, step d and code words; `slow` marks blocks that must be
+// redone on the reference path.
+template <int MODE, int RULE>
+__device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTables& tb, int n6,
+                                           int n4, bool& slow, uint32_t& s, float& d,
+                                           uint32_t& w0, uint32_t& w1, float& bmax) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) m = max3_abs(m, x[i], x[i + 1]);
+  bmax = m;
+  const uint32_t bb = __float_as_uint(m);
+  const int e = (int)(bb >> 23);
+  const f32x2 T = tb.T[(bb >> 16) & 0x7Fu];
+  const float sig6 = fminf(__builtin_amdgcn_ldexpf(T.x, e - n6), 448.0f);
+  const float sig4 = MODE == NVFP4_FOUR_OVER_SIX
+                         ? fminf(__builtin_amdgcn_ldexpf(T.y, e - n4), 448.0f) : 0.0f;
+  const uint32_t sp = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sig6, sig4, 0, false);
+  const uint32_t s6 = sp & 0xFFu;
+  const f32x2 D6 = tb.D[s6];
+  slow = e == 0;
+  const float err6 = fast_candidate<RULE>(x, D6.y, D6.x, w0, w1);
+  s = s6;
+  d = D6.x;
+  if (MODE == NVFP4_FOUR_OVER_SIX) {
+#if NVFP4_SPLIT_CANDIDATES
+    __builtin_amdgcn_sched_barrier(0);   // keep the two trials apart: fewer live registers
+#endif
+    const uint32_t s4 = (sp >> 8) & 0xFFu;
+    const f32x2 D4 = tb.D[s4];
+    slow = slow || m * D4.y > 5.0f;
+    uint32_t a4, b4;
+    const float err4 = fast_candidate<RULE>(x, D4.y, D4.x, a4, b4);
+    if (err4 < err6) { s = s4; d = D4.x; w0 = a4; w1 = b4; }
+  }
+}
+
+__device__ __forceinline__ void unpack16(const uint4& p0, const uint4& p1, float (&x)[16]) {
   const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-  float x[16];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     x[2 * k] = bf16_lo(w[k]);
     x[2 * k + 1] = bf16_hi(w[k]);
   }
-  float bmax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(x[i]));
+}
 
-  float xh6[16], xh4[16];
-  uint32_t s6, a6, b6;
-  const float err6 = run_candidate<RULE, FQ>(x, bmax, alpha, 6.0f * alpha, 7u, s6, a6, b6, xh6);
-  uint32_t s = s6, c0 = a6, c1 = b6;
-  bool four = false;
-  if (MODE == NVFP4_FOUR_OVER_SIX) {
-    uint32_t s4, a4, b4;
-    const float err4 = run_candidate<RULE, FQ>(x, bmax, alpha, 4.0f * alpha, 6u, s4, a4, b4, xh4);
-    four = err4 < err6;            // ties keep 6
-    if (four) { s = s4; c0 = a4; c1 = b4; }
+// Dequantized bf16 of one block from its codes and step: 8 words (two elements each).
+__device__ __forceinline__ void dequant_bf16(uint32_t w0, uint32_t w1, float d, uint32_t (&y)[8]) {
+#define NVFP4_DQ(J, W, SEL)                                                              \
+  {                                                                                      \
+    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(W, 1.0f, SEL);             \
+    const f32x2 q = {v.x * d, v.y * d};                                                  \
+    y[J] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, bf16x2));             \
   }
-  if (FQ) {
-    uint32_t y[8];
+  NVFP4_DQ(0, w0, 0) NVFP4_DQ(1, w0, 1) NVFP4_DQ(2, w0, 2) NVFP4_DQ(3, w0, 3)
+  NVFP4_DQ(4, w1, 0) NVFP4_DQ(5, w1, 1) NVFP4_DQ(6, w1, 2) NVFP4_DQ(7, w1, 3)
+#undef NVFP4_DQ
+}
+
+// Grid: x = workgroups per tensor (grid-stride over units of K blocks), y = tensor.
+// Each lane owns K consecutive blocks per step; the next step's loads are issued before
+// the current step's arithmetic.
+template <int MODE, int RULE, bool FQ>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
+    const uint4* __restrict__ in, int64_t nblk, const float* __restrict__ amax,
+    uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
+    float* __restrict__ alpha_out) {
+  constexpr int K = NVFP4_UNIT_BLOCKS;
+  __shared__ BlockTables tb;
+  const int64_t t = blockIdx.y;
+  const uint32_t abits = __float_as_uint(amax[t]) & 0x7FFFFFFFu;
+  const bool poison = abits >= 0x7F800000u;
+  const float alpha =
+      poison ? 0.0f : __uint_as_float(abits) / (MODE == NVFP4_FOUR_OVER_SIX ? kC6x256 : kC6x448);
+  // alpha_out (distinct from amax) is written by the first lane of each tensor
+  if (alpha_out && blockIdx.x == 0 && threadIdx.x == 0)
+    alpha_out[t] = poison ? __uint_as_float(0x7FC00000u) : alpha;
+
+  const int64_t nunits = (nblk + K - 1) / K;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t base = t * nblk;                 // first block of this tensor
+  int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+
+  if (poison) {                                  // non-finite input or amax
+    for (; u < nunits; u += stride) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float lo = four ? xh4[2 * k] : xh6[2 * k];
-      const float hi = four ? xh4[2 * k + 1] : xh6[2 * k + 1];
-      y[k] = bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+      for (int k = 0; k < K; ++k) {
+        const int64_t b = u * K + k;
+        if (b < nblk) {
+          if (FQ) {
+            const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+            out[2 * (base + b)] = nan4;
+            out[2 * (base + b) + 1] = nan4;
+          } else {
+            codes[base + b] = make_uint2(0u, 0u);
+            scales[base + b] = 0x7F;
+          }
+        }
+      }
     }
-    out[2 * g] = make_uint4(y[0], y[1], y[2], y[3]);
-    out[2 * g + 1] = make_uint4(y[4], y[5], y[6], y[7]);
-  } else {
-    codes[g] = make_uint2(c0, c1);
-    scales[g] = (uint8_t)s;
+    return;
+  }
+
+  int n6, n4;
+  build_tables<MODE>(tb, alpha, n6, n4);
+  __syncthreads();
+  const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
+
+  constexpr int PF = NVFP4_PREFETCH;            // units in flight ahead of the one computed
+  uint4 ring[PF][2 * K];
+  auto load_unit = [&](uint4 (&dst)[2 * K], int64_t uu) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t b = uu * K + k;
+      if (K == 1 || b < nblk) {
+        dst[2 * k] = in[2 * (base + b)];
+        dst[2 * k + 1] = in[2 * (base + b) + 1];
+      } else {
+        dst[2 * k] = make_uint4(0u, 0u, 0u, 0u);
+        dst[2 * k + 1] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+#pragma unroll
+  for (int f = 0; f < PF; ++f)
+    if (u + f * stride < nunits) load_unit(ring[f], u + f * stride);
+  for (; u < nunits; u += stride) {
+    uint4 cur[2 * K];
+#pragma unroll
+    for (int k = 0; k < 2 * K; ++k) cur[k] = ring[0][k];
+#pragma unroll
+    for (int f = 0; f + 1 < PF; ++f)
+#pragma unroll
+      for (int k = 0; k < 2 * K; ++k) ring[f][k] = ring[f + 1][k];
+    if (K == 1)          // always in bounds: past the end it reloads the last unit
+      load_unit(ring[PF - 1], min(u + PF * stride, nunits - 1));
+    else if (u + PF * stride < nunits)
+      load_unit(ring[PF - 1], u + PF * stride);
+
+    uint32_t sc[K], w0[K], w1[K];
+    float dq[K], bm[K];
+    bool slow[K];
+    bool any_slow = false;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      float x[16];
+      unpack16(cur[2 * k], cur[2 * k + 1], x);
+      fast_block<MODE, RULE>(x, tb, n6, n4, slow[k], sc[k], dq[k], w0[k], w1[k], bm[k]);
+      slow[k] = slow[k] || tiny_alpha;
+      any_slow = any_slow || slow[k];
+    }
+    if (any_slow) {                  // rare: redo those blocks on the reference path
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if (slow[k]) {
+          const RefOut o = ref_block<MODE, RULE>(
+              reinterpret_cast<const uint16_t*>(in + 2 * (base + u * K + k)), bm[k], alpha);
+          sc[k] = o.s;
+          dq[k] = o.d;
+          w0[k] = o.w0;
+          w1[k] = o.w1;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int64_t b = u * K + k;
+      if (K > 1 && b >= nblk) break;
+      if (FQ) {
+        uint32_t y[8];
+        dequant_bf16(w0[k], w1[k], dq[k], y);
+        out[2 * (base + b)] = make_uint4(y[0], y[1], y[2], y[3]);
+        out[2 * (base + b) + 1] = make_uint4(y[4], y[5], y[6], y[7]);
+      } else {
+        codes[base + b] = make_uint2(w0[k], w1[k]);
+        scales[base + b] = (uint8_t)sc[k];
+      }
+    }
   }
 }
 
@@ -294,19 +531,23 @@ nvfp4_status check_common(const uint16_t* in, const Shape& s, int block, int mod
 
 hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStream_t stream) {
   const int64_t chunks = s.n / 8;
-  const int64_t want = (chunks + kThreads * 4 - 1) / (kThreads * 4);
-  const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, 4096 / s.E + 1));
+  const int64_t want = (chunks + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
+  const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, kAmaxWGs / s.E));
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((s.E + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                      stream, acc, s.E);
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(in), chunks, acc);
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads), 0,
+                     stream, reinterpret_cast<const uint4*>(in), chunks, acc);
   return hipGetLastError();
 }
 
 template <int MODE, int RULE, bool FQ>
 void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, uint8_t* codes,
                        uint8_t* scales, uint16_t* out, float* alpha_out, hipStream_t stream) {
-  const dim3 grid((unsigned)((s.nblk + kThreads - 1) / kThreads), (unsigned)s.E);
+  const int64_t units = (s.nblk + NVFP4_UNIT_BLOCKS - 1) / NVFP4_UNIT_BLOCKS;
+  const int64_t want = (units + kThreads - 1) / kThreads;
+  const int64_t per_tensor =
+      std::max<int64_t>(1, std::min<int64_t>(want, NVFP4_BLOCK_WGS / s.E));
+  const dim3 grid((unsigned)per_tensor, (unsigned)s.E);
   hipLaunchKernelGGL((quantize_kernel<MODE, RULE, FQ>), grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(in), s.nblk, amax,
                      reinterpret_cast<uint2*>(codes), scales, reinterpret_cast<uint4*>(out),
