@@ -3,17 +3,23 @@
 One step is one pass of the whole hot path over one synthetic tensor: the amax
 pass (clear + streaming max), then the block pass (alpha, both candidate scales,
 FP4 rounding, error, selection, packed codes + E4M3 scales).  The step calls the
-two C-ABI entry points nvfp4_amax and nvfp4_quantize_from_amax back to back --
-the same kernels, in the same order, as nvfp4_quantize -- so that HIP events on
-the launch stream can time each pass inside the timed region.
+C-ABI entry points nvfp4_amax and nvfp4_quantize_from_amax back to back -- the
+kernels of nvfp4_quantize, in the same order.
 
 Default workload: the 4096 x 14336 bf16 weight (N(0, 0.02^2), 0.1 % of entries
 x20), Four Over Six with the MSE rule, packed output.  Inputs are generated once
-on the host, copied to HBM and rotated over enough copies that every step reads
-data that the 256 MB Infinity Cache no longer holds.
+on the host, copied to HBM and rotated over enough copies that each step starts
+on data the 256 MB Infinity Cache no longer holds.
 
-Printed: one JSON line (see the keys below).  value = algorithmic bytes of a step
-(2 B/elem amax read + 2.5625 B/elem block pass) / step time, in GB/s.
+Timing:
+  * timed region: K steps captured as one HIP graph and replayed once, bracketed
+    by torch.cuda.synchronize() (so host launch overhead is not timed); gives
+    ms_per_step and value = algorithmic bytes per step / step time
+    (2 B/elem amax read + 2.5625 B/elem block pass, or 4 B/elem fake-quant).
+  * per-kernel legs: graphs of back-to-back launches of one pass over rotating
+    cold buffers, HIP events recorded on the launch stream before and after the
+    replay; the average launch of the block pass is the roofline figure.
+Printed: one JSON line.
 """
 from __future__ import annotations
 
@@ -48,30 +54,32 @@ def source_digest() -> str:
 
 
 def read_counters(workload, mode, rule):
-    """HBM traffic per dispatch of the block-pass kernel from the committed rocprofv3
-    counter summary, or None when absent or taken on a different kernel source."""
+    """HBM bytes per dispatch of the block-pass kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy's reading), or None when
+    absent or taken on a different kernel source."""
     if not os.path.exists(COUNTERS):
         return None
-    want = "%s %s %s" % (workload, mode, rule)
+    want = "%s,%s,%s" % (workload, mode, rule)
     for line in open(COUNTERS):
         if line.startswith("TRAFFIC "):
             f = dict(kv.split("=", 1) for kv in line.split()[1:])
-            if f.get("source") == source_digest() and f.get("case", "").replace(",", " ") == want:
-                return float(f["bytes_per_dispatch"])
+            if f.get("source") == source_digest() and f.get("case") == want:
+                return int(float(f["bytes_per_dispatch"]))
     return None
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="weight")
     ap.add_argument("--mode", default="four_over_six")
     ap.add_argument("--rule", default="mse")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="timed steps only (for rocprofv3 runs): no extra legs")
+                    help="counter runs: add a plain 256 MiB device copy (calibration), "
+                         "skip the CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -93,8 +101,8 @@ def main():
     x_cpu = W.generate(wl.name)
     N = x_cpu.numel()
     E = wl.shape[0] if len(wl.shape) == 3 else 1
-    step_bpe = AMAX_BPE + (FQ_BPE if fq else PACKED_BPE)
     pass_bpe = FQ_BPE if fq else PACKED_BPE
+    step_bpe = AMAX_BPE + pass_bpe
     one_set = N * 2 + (N * 2 if fq else N // 2 + N // 16)
     R = max(2, math.ceil(3 * MALL_BYTES / one_set) + 1)
     log("[bench] %d rotating buffer sets of %.1f MB" % (R, one_set / 1e6))
@@ -110,41 +118,89 @@ def main():
     amaxs = [torch.empty(E, dtype=torch.float32, device=dev) for _ in range(R)]
     alphas = [torch.empty(E, dtype=torch.float32, device=dev) for _ in range(R)]
 
-    def block_pass(i, mode, rule):
+    def block_pass(i, mode=args.mode, rule=args.rule):
         if fq:
             nv.fakequant_from_amax(xs[i], amaxs[i], mode, rule, out=outs[i], alpha=alphas[i])
         else:
             nv.quantize_from_amax(xs[i], amaxs[i], mode, rule, codes=outs[i][0],
                                   scales=outs[i][1], alpha=alphas[i])
 
-    def step(i):
+    def amax_pass(i):
         nv.amax(xs[i], out=amaxs[i])
-        block_pass(i, args.mode, args.rule)
 
-    for s in range(args.warmup):
-        step(s % R)
-    torch.cuda.synchronize()
+    def step(i):
+        amax_pass(i)
+        block_pass(i)
 
-    # ---- timed region: K steps, HIP events between the two passes on the launch stream
+    def dynamic_call(i):
+        if fq:
+            nv.fakequant(xs[i], args.mode, args.rule, out=outs[i], alpha=alphas[i])
+        else:
+            nv.quantize(xs[i], args.mode, args.rule, codes=outs[i][0], scales=outs[i][1],
+                        alpha=alphas[i])
+
+    def capture(fn, count):
+        """One HIP graph of `count` back-to-back calls fn(0), fn(1), ... (buffers mod R)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(min(count, R)):
+                fn(i % R)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                fn(i % R)
+        return g
+
+    def replay_avg_us(g, count, reps=3):
+        """Median over reps of (events around one replay) / count, in microseconds."""
+        out = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) * 1e3 / count)
+        return float(np.median(out))
+
+    # ---- timed region: K steps in one graph, replayed once
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    log("[bench] capturing %d warmup + %d timed steps" % (args.warmup, K))
+    g_warm = capture(step, max(1, args.warmup))
+    g_steps = capture(step, K)
+    g_warm.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(K):
-        i = s % R
-        ev[s][0].record()
-        nv.amax(xs[i], out=amaxs[i])
-        ev[s][1].record()
-        block_pass(i, args.mode, args.rule)
-        ev[s][2].record()
+    g_steps.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / K
-    amax_us = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in ev])
-    pass_us = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in ev])
     value = step_bpe * N / (ms_step * 1e-3) / 1e9
+    del g_warm, g_steps
+    log("[bench] timed region: %.1f us/step" % (ms_step * 1e3))
 
-    pass_gbps = pass_bpe * N / (pass_us.mean() * 1e-6) / 1e9
+    # ---- per-kernel legs: back-to-back launches of one pass over cold rotating buffers
+    B = max(4 * R, 32)
+    for i in range(R):
+        amax_pass(i)
+    torch.cuda.synchronize()
+    legs = {}
+    for name, fn in (("block", block_pass),
+                     ("rtn6_block", lambda i: block_pass(i, "rtn6", "mse")),
+                     ("block_again", block_pass),          # 4/6 once more: drift check
+                     ("amax", amax_pass),
+                     ("dynamic_entry_point", dynamic_call)):
+        g = capture(fn, B)
+        legs[name] = replay_avg_us(g, B)
+        del g
+        log("[bench] leg %s: %.2f us per launch" % (name, legs[name]))
+    t_block = min(legs["block"], legs["block_again"])
+    t_rtn6 = legs["rtn6_block"]
+    block_gbps = pass_bpe * N / (t_block * 1e-6) / 1e9
+
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -153,25 +209,43 @@ def main():
         "config": {"workload": "%s: %s" % (wl.name, wl.description), "shape": list(wl.shape),
                    "elements": N, "mode": args.mode, "rule": args.rule,
                    "output": "fakequant" if fq else "packed", "block": 16,
-                   "rotating_buffer_sets": R},
-    }
-    traffic = read_counters(wl.name, args.mode, args.rule)
-    result["roofline"] = {
-        "bound": "hbm", "achieved": round(pass_gbps, 1), "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s", "frac": round(pass_gbps / HBM_PEAK_GBPS, 4),
-        "traffic": traffic,
-        "kernel": "quantize_kernel<%s,%s,%s>" % (args.mode, args.rule, "fq" if fq else "packed"),
-        "bytes_per_launch": int(pass_bpe * N), "avg_launch_us": round(float(pass_us.mean()), 2),
-    }
-    result["passes"] = {
-        "amax": {"avg_us": round(float(amax_us.mean()), 2), "p50_us": round(float(np.median(amax_us)), 2),
-                 "GBps": round(AMAX_BPE * N / (amax_us.mean() * 1e-6) / 1e9, 1)},
-        "block": {"avg_us": round(float(pass_us.mean()), 2), "p50_us": round(float(np.median(pass_us)), 2),
-                  "p10_us": round(float(np.percentile(pass_us, 10)), 2),
-                  "p90_us": round(float(np.percentile(pass_us, 90)), 2),
-                  "GBps": round(pass_gbps, 1), "frac_hbm": round(pass_gbps / HBM_PEAK_GBPS, 4)},
+                   "rotating_buffer_sets": R, "timed_as": "one HIP graph of K steps"},
+        "roofline": {
+            "bound": "hbm", "achieved": round(block_gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(block_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": read_counters(wl.name, args.mode, args.rule),
+            "kernel": "quantize_kernel<%s,%s,%s>" % (args.mode, args.rule,
+                                                     "fakequant" if fq else "packed"),
+            "bytes_per_launch": int(pass_bpe * N), "avg_launch_us": round(t_block, 2),
+            "launches_timed": B, "buffers": "cold (rotating)",
+        },
+        "passes": {
+            "block": {"avg_us": round(t_block, 2), "GBps": round(block_gbps, 1),
+                      "frac_hbm": round(block_gbps / HBM_PEAK_GBPS, 4)},
+            "rtn6_block": {"avg_us": round(t_rtn6, 2),
+                           "GBps": round(pass_bpe * N / (t_rtn6 * 1e-6) / 1e9, 1)},
+            "amax": {"avg_us": round(legs["amax"], 2),
+                     "GBps": round(AMAX_BPE * N / (legs["amax"] * 1e-6) / 1e9, 1)},
+            "dynamic_entry_point": {"avg_us": round(legs["dynamic_entry_point"], 2)},
+        },
+        "overhead_4over6_vs_rtn6": round(t_block / t_rtn6 - 1.0, 4),
     }
 
+    # ---- device copy bandwidth (read + write of 1 GiB), a second denominator
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 10 * 2 * src.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
+    result["copy_GBps"] = round(copy_gbps, 1)
+    result["passes"]["block"]["frac_copy"] = round(block_gbps / copy_gbps, 4)
+    del src, dst
     if args.profile:
         # a plain device copy of known size (256 MiB read + 256 MiB written), so that a
         # counter run of this command can calibrate FETCH_SIZE / WRITE_SIZE against it
@@ -180,64 +254,6 @@ def main():
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
-    else:
-        # ---- block pass alone on cold buffers (no amax pass before it), and rtn6 on the same
-        def time_pass(mode, rule, reps):
-            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-            for r in range(reps):
-                i = r % R
-                evs[r][0].record()
-                block_pass(i, mode, rule)
-                evs[r][1].record()
-            torch.cuda.synchronize()
-            return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-        for i in range(R):
-            nv.amax(xs[i], out=amaxs[i])
-        torch.cuda.synchronize()
-        reps = max(K, 2 * R)
-        cold46 = time_pass(args.mode, args.rule, reps)
-        cold6 = time_pass("rtn6", "mse", reps)
-        cold46b = time_pass(args.mode, args.rule, reps)
-        t46 = float(np.median(np.concatenate([cold46, cold46b])))
-        t6 = float(np.median(cold6))
-        result["passes"]["block_cold"] = {"p50_us": round(t46, 2),
-                                          "GBps": round(pass_bpe * N / (t46 * 1e-6) / 1e9, 1)}
-        result["passes"]["rtn6_block_cold"] = {"p50_us": round(t6, 2),
-                                               "GBps": round(pass_bpe * N / (t6 * 1e-6) / 1e9, 1)}
-        result["overhead_4over6_vs_rtn6"] = round(t46 / t6 - 1.0, 4)
-
-        # ---- the single-call dynamic entry point end to end (4 launches)
-        evs = []
-        for r in range(reps):
-            i = r % R
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            if fq:
-                nv.fakequant(xs[i], args.mode, args.rule, out=outs[i], alpha=alphas[i])
-            else:
-                nv.quantize(xs[i], args.mode, args.rule, codes=outs[i][0], scales=outs[i][1],
-                            alpha=alphas[i])
-            b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        e2e = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-        result["passes"]["dynamic_entry_point"] = {"p50_us": round(float(np.median(e2e)), 2)}
-
-        # ---- device copy bandwidth (read + write), a second denominator
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(10):
-            dst.copy_(src)
-        b.record()
-        torch.cuda.synchronize()
-        copy_gbps = 10 * 2 * src.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
-        result["copy_GBps"] = round(copy_gbps, 1)
-        result["passes"]["block"]["frac_copy"] = round(pass_gbps / copy_gbps, 4)
         del src, dst
 
     if not args.no_cpu_baseline and not args.profile:
@@ -248,8 +264,8 @@ def main():
 
 def cpu_baseline(x_cpu, wl, args, step_bpe):
     """The CPU oracle (untuned, test infrastructure) on a bounded sample of the workload:
-    the leading rows of the tensor (of the first experts for batched workloads), the whole
-    hot path (amax + block pass), on the host's cores."""
+    the whole hot path (amax + block pass) on the leading rows of the tensor (the first
+    experts for batched workloads), on the host's cores; median of repeated runs."""
     import numpy as np
 
     import oracle

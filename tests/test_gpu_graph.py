@@ -1,0 +1,79 @@
+"""HIP graph capture of the library's launches (GPU).
+
+The library launches only kernels (its accumulator clear is a kernel, not a memset), so a
+call can be captured into a HIP graph and replayed.  Each graph here is replayed several
+times with other eager work and synchronizations between the replays, and every replay
+is compared with the eager result."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_amax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_block_scaled_amax_amd as m
+    m.lib()
+    return m
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+@pytest.mark.parametrize("shape", [(96, 448), (3, 40, 160)], ids=["2d", "batched"])
+@pytest.mark.parametrize("mode,rule", [("rtn6", "mse"), ("four_over_six", "mae")])
+def test_graph_replays_match_eager(nv, orc, shape, mode, rule):
+    x = W.generate("large", shape).cuda()
+    other = W.generate("weight", shape).cuda()
+    E = shape[0] if len(shape) == 3 else 1
+    lead = shape[:-2]
+    codes = torch.empty(lead + (shape[-2], shape[-1] // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(lead + (shape[-2], shape[-1] // 16), dtype=torch.uint8, device="cuda")
+    alpha = torch.empty(E, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    alpha_y = torch.empty(E, dtype=torch.float32, device="cuda")
+    am = torch.empty(E, dtype=torch.float32, device="cuda")
+    codes2, scales2, alpha2 = torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(alpha)
+
+    def work():
+        nv.quantize(x, mode, rule, codes=codes, scales=scales, alpha=alpha)
+        nv.fakequant(x, mode, rule, out=y, alpha=alpha_y)
+        nv.amax(x, out=am)
+        nv.quantize_from_amax(x, am, mode, rule, codes=codes2, scales=scales2, alpha=alpha2)
+
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (codes, scales, alpha, y, alpha_y, am, codes2, scales2, alpha2)]
+    g = _capture(work)
+    outs = (codes, scales, alpha, y, alpha_y, am, codes2, scales2, alpha2)
+    for r in range(4):
+        for t in outs:
+            t.zero_()
+        nv.quantize(other, mode, rule)            # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (t, e) in enumerate(zip(outs, ref)):
+            assert torch.equal(t.view(torch.uint8), e.view(torch.uint8)), (r, k)
+    # the eager result itself is the oracle's
+    xb = W.bits(x.cpu())
+    o = orc.quantize(xb, mode, rule)
+    assert np.array_equal(codes.cpu().numpy(), o["codes"])
+    assert np.array_equal(W.bits(y.cpu()), o["y"])
