@@ -133,6 +133,28 @@ nvfp4_status nvfp4_fakequant_from_amax(const uint16_t* in, int64_t E, int64_t ro
                                        nvfp4_rule rule, const float* amax, uint16_t* out,
                                        float* out_alpha, hipStream_t stream);
 
+/* Diagnostics of a packed quantization (dynamic scale, E tensors): the outputs of
+ * nvfp4_quantize_batched plus, per block, the block maximum it was scaled to
+ * (out_qstar [E][rows][cols/16]: 4 or 6, always 6 for rtn6, 0 for a poisoned tensor) and, per
+ * tensor, the number of blocks scaled to 4 (out_count4 [E], cleared by the call).  The Four
+ * Over Six explainer ("Key contributions and results") expects blocks with large near-max
+ * values to pick 4; this shows how often that happens on a given tensor. */
+nvfp4_status nvfp4_quantize_diag(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
+                                 int block, nvfp4_mode mode, nvfp4_rule rule,
+                                 uint8_t* out_codes, uint8_t* out_scales, float* out_alpha,
+                                 uint8_t* out_qstar, uint32_t* out_count4, hipStream_t stream);
+
+/* Dequantize packed NVFP4 to bf16 (for W4A16-style consumers that store 4-bit weights; the
+ * Nemotron 3.5 Lightning NVFP4 news page, "two-stage QAD", quantizes the student to W4A16):
+ *   out = bf16(RN(val(code) * RN(dec(scale) * alpha[e])))
+ * which is bit-identical to the fake-quant output of the tensor that produced the codes.
+ * codes [E][rows][cols/2] (8-byte aligned), scales [E][rows][cols/16], alpha [E] (device),
+ * out [E][rows][cols] bf16 (16-byte aligned).  A NaN alpha or a NaN scale byte (0x7F, 0xFF)
+ * gives 0x7FC0 for the whole block.  One launch. */
+nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* alpha,
+                              int64_t E, int64_t rows, int64_t cols, uint16_t* out,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

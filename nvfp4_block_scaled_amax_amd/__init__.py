@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["quantize", "fakequant", "amax", "quantize_from_amax", "fakequant_from_amax",
-           "lib", "NVFP4Error", "MODES", "RULES", "LIB_PATH"]
+           "dequantize", "quantize_diag", "lib", "NVFP4Error", "MODES", "RULES", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_amax.so")
 MODES = {"rtn6": 0, "four_over_six": 1}
@@ -56,7 +56,9 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_fakequant_batched.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P]
         L.nvfp4_quantize_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P]
         L.nvfp4_fakequant_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
-        for name in ("nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
+        L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i64, P, P]
+        L.nvfp4_quantize_diag.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P, P]
+        for name in ("nvfp4_quantize_diag", "nvfp4_dequantize", "nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
                      "nvfp4_fakequant_batched", "nvfp4_quantize_from_amax",
                      "nvfp4_fakequant_from_amax"):
             getattr(L, name).restype = i32
@@ -140,6 +142,21 @@ def quantize(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=None, s
     return codes, scales, alpha
 
 
+def quantize_diag(x: torch.Tensor, mode="four_over_six", rule="mse"):
+    """Packed NVFP4 (dynamic scale) plus diagnostics -> (codes, scales, alpha, qstar, count4):
+    qstar uint8 [..., rows, cols/16] is 4 or 6 per block, count4 int32 [E] counts the blocks
+    scaled to 4."""
+    E, rows, cols, batched = _dims(x)
+    codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, None, None, None)
+    qstar = torch.empty_like(scales)
+    count4 = torch.empty(E, dtype=torch.int32, device=x.device)
+    st = lib().nvfp4_quantize_diag(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                   _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(qstar),
+                                   _ptr(count4), _stream(x))
+    _check(st, "nvfp4_quantize_diag")
+    return codes, scales, alpha, qstar, count4
+
+
 def fakequant(x: torch.Tensor, mode="four_over_six", rule="mse", *, out=None, alpha=None):
     """bf16 quantize-dequantize with a dynamic per-tensor scale -> (y, alpha).
     out may be x itself (in place)."""
@@ -180,3 +197,24 @@ def fakequant_from_amax(x: torch.Tensor, amax_: torch.Tensor, mode="four_over_si
                                          _ptr(amax_), _ptr(out), _ptr(alpha), _stream(x))
     _check(st, "nvfp4_fakequant_from_amax")
     return out, alpha
+
+
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, *, out=None):
+    """Packed NVFP4 -> bf16: codes uint8 [rows, cols/2] or [E, rows, cols/2], scales uint8
+    [..., rows, cols/16], alpha float32 [E]; equal to the fake-quant output."""
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or alpha.dtype != torch.float32:
+        raise TypeError("codes and scales must be uint8, alpha float32")
+    if not (codes.is_cuda and scales.is_cuda and alpha.is_cuda):
+        raise ValueError("codes, scales and alpha must be GPU tensors")
+    if not (codes.is_contiguous() and scales.is_contiguous() and alpha.is_contiguous()):
+        raise ValueError("codes, scales and alpha must be contiguous")
+    if codes.dim() not in (2, 3):
+        raise ValueError("codes must be [rows, cols/2] or [E, rows, cols/2]")
+    E = codes.shape[0] if codes.dim() == 3 else 1
+    rows, cols = codes.shape[-2], codes.shape[-1] * 2
+    if tuple(scales.shape) != tuple(codes.shape[:-1]) + (cols // 16,) or alpha.numel() != E:
+        raise ValueError("scales must be [..., rows, cols/16] and alpha [E]")
+    out = _out(out, tuple(codes.shape[:-1]) + (cols,), torch.bfloat16, codes)
+    _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(alpha), E, rows, cols,
+                                  _ptr(out), _stream(codes)), "nvfp4_dequantize")
+    return out

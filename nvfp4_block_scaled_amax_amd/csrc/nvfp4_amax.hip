@@ -71,9 +71,12 @@ __device__ __forceinline__ float e2m1_value_of(uint32_t m) {
 }
 
 // ----------------------------------------------------------------------------- kernels
-__global__ void clear_kernel(uint32_t* __restrict__ acc, int64_t E) {
+__global__ void clear_kernel(uint32_t* __restrict__ acc, uint32_t* __restrict__ acc2, int64_t E) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < E) acc[i] = 0u;
+  if (i < E) {
+    acc[i] = 0u;
+    if (acc2) acc2[i] = 0u;
+  }
 }
 
 // Max of two packed unsigned 16-bit lanes (v_pk_max_u16).
@@ -106,26 +109,28 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Grid: x = workgroups per tensor, y = tensor.  Few, large workgroups (one atomic each:
-// same-address atomics serialize, so their count is kept near the CU count), each
-// striding over the tensor's 16-byte chunks (8 bf16 values) with 8 loads in flight.
+// same-address atomics serialize, so their count is kept near the CU count).  Each lane
+// reads 8 consecutive 16-byte chunks (128 bytes, 64 bf16 values) per step, the workgroups
+// striding over the tensor.
 constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxWGs = 256;
+constexpr int kAmaxChunks = 8;
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restrict__ in,
                                                             int64_t chunks,
                                                             uint32_t* __restrict__ acc) {
-  constexpr int U = 8;
+  constexpr int C = kAmaxChunks;
   const uint4* p = in + (int64_t)blockIdx.y * chunks;
-  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-  int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads * C;
+  int64_t i = ((int64_t)blockIdx.x * kAmaxThreads + threadIdx.x) * C;
   uint32_t m = 0;
-  for (; i + (U - 1) * stride < chunks; i += U * stride) {
-    uint4 v[U];
+  for (; i + C <= chunks; i += stride) {
+    uint4 v[C];
 #pragma unroll
-    for (int k = 0; k < U; ++k) v[k] = p[i + k * stride];
+    for (int k = 0; k < C; ++k) v[k] = p[i + k];
 #pragma unroll
-    for (int k = 0; k < U; ++k) m = mag_max8(m, v[k]);
+    for (int k = 0; k < C; ++k) m = mag_max8(m, v[k]);
   }
-  for (; i < chunks; i += stride) m = mag_max8(m, p[i]);
+  for (; i < chunks; ++i) m = mag_max8(m, p[i]);   // the one lane whose chunks run past the end
   // the larger of the two 16-bit magnitudes, as the bits of a binary32 value
   m = max(m & 0xFFFFu, m >> 16) << 16;
   m = wave_max_u32(m);
@@ -210,6 +215,7 @@ __device__ __forceinline__ float ref_candidate(const uint16_t* __restrict__ xb, 
 struct RefOut {
   uint32_t s, w0, w1;
   float d;
+  bool four;   // the block was scaled to 4
 };
 
 // Returned by value (in registers): outputs passed by reference would make the caller
@@ -218,12 +224,13 @@ template <int MODE, int RULE>
 __device__ __noinline__ RefOut ref_block(const uint16_t* __restrict__ xb, float bmax,
                                          float alpha) {
   RefOut o;
+  o.four = false;
   const float err6 = ref_candidate<RULE>(xb, bmax, alpha, 6.0f * alpha, 7u, o.s, o.d, o.w0, o.w1);
   if (MODE == NVFP4_FOUR_OVER_SIX) {
     uint32_t s4, a4, b4;
     float d4;
     const float err4 = ref_candidate<RULE>(xb, bmax, alpha, 4.0f * alpha, 6u, s4, d4, a4, b4);
-    if (err4 < err6) { o.s = s4; o.d = d4; o.w0 = a4; o.w1 = b4; }   // ties keep 6
+    if (err4 < err6) { o.s = s4; o.d = d4; o.w0 = a4; o.w1 = b4; o.four = true; }   // ties keep 6
   }
   return o;
 }
@@ -315,7 +322,7 @@ __device__ __forceinline__ void build_tables(BlockTables& tb, float alpha, int& 
 template <int MODE, int RULE>
 __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTables& tb, int n6,
                                            int n4, bool& slow, uint32_t& s, float& d,
-                                           uint32_t& w0, uint32_t& w1, float& bmax) {
+                                           uint32_t& w0, uint32_t& w1, float& bmax, bool& four) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; i += 2) m = max3_abs(m, x[i], x[i + 1]);
@@ -330,6 +337,7 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
   const uint32_t s6 = sp & 0xFFu;
   const f32x2 D6 = tb.D[s6];
   slow = e == 0;
+  four = false;
   const float err6 = fast_candidate<RULE>(x, D6.y, D6.x, w0, w1);
   s = s6;
   d = D6.x;
@@ -342,7 +350,7 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
     slow = slow || m * D4.y > 5.0f;
     uint32_t a4, b4;
     const float err4 = fast_candidate<RULE>(x, D4.y, D4.x, a4, b4);
-    if (err4 < err6) { s = s4; d = D4.x; w0 = a4; w1 = b4; }
+    if (err4 < err6) { s = s4; d = D4.x; w0 = a4; w1 = b4; four = true; }   // ties keep 6
   }
 }
 
@@ -370,13 +378,14 @@ __device__ __forceinline__ void dequant_bf16(uint32_t w0, uint32_t w1, float d, 
 
 // Grid: x = workgroups per tensor (grid-stride over units of K blocks), y = tensor.
 // Each lane owns K consecutive blocks per step; the next step's loads are issued before
-// the current step's arithmetic.
-template <int MODE, int RULE, bool FQ>
+// the current step's arithmetic.  DIAG (packed output only) also writes, per block, the
+// block maximum it was scaled to (4 or 6) and counts the blocks scaled to 4 per tensor.
+template <int MODE, int RULE, bool FQ, bool DIAG>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     const uint4* __restrict__ in, int64_t nblk, const float* __restrict__ amax,
     uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
-    float* __restrict__ alpha_out) {
+    float* __restrict__ alpha_out, uint8_t* __restrict__ qstar, uint32_t* __restrict__ count4) {
   constexpr int K = NVFP4_UNIT_BLOCKS;
   __shared__ BlockTables tb;
   const int64_t t = blockIdx.y;
@@ -406,12 +415,14 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
           } else {
             codes[base + b] = make_uint2(0u, 0u);
             scales[base + b] = 0x7F;
+            if (DIAG) qstar[base + b] = 0;
           }
         }
       }
     }
     return;
   }
+  uint32_t n_four = 0;   // DIAG: blocks of this lane scaled to 4
 
   int n6, n4;
   build_tables<MODE>(tb, alpha, n6, n4);
@@ -451,13 +462,13 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 
     uint32_t sc[K], w0[K], w1[K];
     float dq[K], bm[K];
-    bool slow[K];
+    bool slow[K], four[K];
     bool any_slow = false;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       float x[16];
       unpack16(cur[2 * k], cur[2 * k + 1], x);
-      fast_block<MODE, RULE>(x, tb, n6, n4, slow[k], sc[k], dq[k], w0[k], w1[k], bm[k]);
+      fast_block<MODE, RULE>(x, tb, n6, n4, slow[k], sc[k], dq[k], w0[k], w1[k], bm[k], four[k]);
       slow[k] = slow[k] || tiny_alpha;
       any_slow = any_slow || slow[k];
     }
@@ -471,6 +482,7 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
           dq[k] = o.d;
           w0[k] = o.w0;
           w1[k] = o.w1;
+          four[k] = o.four;
         }
       }
     }
@@ -486,8 +498,57 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
       } else {
         codes[base + b] = make_uint2(w0[k], w1[k]);
         scales[base + b] = (uint8_t)sc[k];
+        if (DIAG) {
+          qstar[base + b] = four[k] ? 4 : 6;
+          n_four += four[k] ? 1u : 0u;
+        }
       }
     }
+  }
+  if (DIAG) {            // one integer atomic per workgroup: exact, order-free
+    __shared__ uint32_t wsum[kThreads / 64];
+    uint32_t v = n_four;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t tot = 0;
+      for (int w = 0; w < kThreads / 64; ++w) tot += wsum[w];
+      if (tot) atomicAdd(count4 + t, tot);
+    }
+  }
+}
+
+// Dequantize: packed codes + scale bytes + alpha -> bf16, one block per lane per step.
+// d = RN(dec(s) * alpha) and y = bf16(RN(val(code) * d)): the values the fake-quant output
+// holds for the tensor that was quantized.  A NaN alpha or scale byte gives NaN (0x7FC0).
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint2* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           const float* __restrict__ alpha,
+                                                           int64_t nblk, uint4* __restrict__ out) {
+  const int64_t t = blockIdx.y;
+  const float al = alpha[t];
+  const bool nan_alpha = al != al;
+  const int64_t base = t * nblk;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
+    const uint2 c = codes[base + b];
+    const uint32_t sb = scales[base + b];
+    uint4 y0, y1;
+    if (nan_alpha || (sb & 0x7Fu) == 0x7Fu) {
+      y0 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+      y1 = y0;
+    } else {
+      const float dec = e4m3_to_f32(sb & 0x7Fu);
+      const float d = (sb & 0x80u ? -dec : dec) * al;
+      uint32_t y[8];
+      dequant_bf16(c.x, c.y, d, y);
+      y0 = make_uint4(y[0], y[1], y[2], y[3]);
+      y1 = make_uint4(y[4], y[5], y[6], y[7]);
+    }
+    out[2 * (base + b)] = y0;
+    out[2 * (base + b) + 1] = y1;
   }
 }
 
@@ -529,43 +590,49 @@ nvfp4_status check_common(const uint16_t* in, const Shape& s, int block, int mod
   return NVFP4_OK;
 }
 
-hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStream_t stream) {
+hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStream_t stream,
+                       uint32_t* acc2 = nullptr) {
   const int64_t chunks = s.n / 8;
-  const int64_t want = (chunks + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
+  const int64_t want = (chunks + kAmaxThreads * kAmaxChunks - 1) / (kAmaxThreads * kAmaxChunks);
   const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, kAmaxWGs / s.E));
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((s.E + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     stream, acc, s.E);
+                     stream, acc, acc2, s.E);
   hipLaunchKernelGGL(amax_kernel, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads), 0,
                      stream, reinterpret_cast<const uint4*>(in), chunks, acc);
   return hipGetLastError();
 }
 
-template <int MODE, int RULE, bool FQ>
+template <int MODE, int RULE, bool FQ, bool DIAG>
 void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, uint8_t* codes,
-                       uint8_t* scales, uint16_t* out, float* alpha_out, hipStream_t stream) {
+                       uint8_t* scales, uint16_t* out, float* alpha_out, uint8_t* qstar,
+                       uint32_t* count4, hipStream_t stream) {
   const int64_t units = (s.nblk + NVFP4_UNIT_BLOCKS - 1) / NVFP4_UNIT_BLOCKS;
   const int64_t want = (units + kThreads - 1) / kThreads;
   const int64_t per_tensor =
       std::max<int64_t>(1, std::min<int64_t>(want, NVFP4_BLOCK_WGS / s.E));
   const dim3 grid((unsigned)per_tensor, (unsigned)s.E);
-  hipLaunchKernelGGL((quantize_kernel<MODE, RULE, FQ>), grid, dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((quantize_kernel<MODE, RULE, FQ, DIAG>), grid, dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(in), s.nblk, amax,
                      reinterpret_cast<uint2*>(codes), scales, reinterpret_cast<uint4*>(out),
-                     alpha_out);
+                     alpha_out, qstar, count4);
 }
 
-template <bool FQ>
+template <bool FQ, bool DIAG>
 void launch_quantize(int mode, int rule, const uint16_t* in, const Shape& s, const float* amax,
                      uint8_t* codes, uint8_t* scales, uint16_t* out, float* alpha_out,
-                     hipStream_t stream) {
+                     uint8_t* qstar, uint32_t* count4, hipStream_t stream) {
   if (mode == NVFP4_RTN6) {
-    launch_quantize_t<NVFP4_RTN6, NVFP4_RULE_MSE, FQ>(in, s, amax, codes, scales, out, alpha_out, stream);
+    launch_quantize_t<NVFP4_RTN6, NVFP4_RULE_MSE, FQ, DIAG>(in, s, amax, codes, scales, out,
+                                                            alpha_out, qstar, count4, stream);
   } else if (rule == NVFP4_RULE_MSE) {
-    launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MSE, FQ>(in, s, amax, codes, scales, out, alpha_out, stream);
+    launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MSE, FQ, DIAG>(
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stream);
   } else if (rule == NVFP4_RULE_MAE) {
-    launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAE, FQ>(in, s, amax, codes, scales, out, alpha_out, stream);
+    launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAE, FQ, DIAG>(
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stream);
   } else {
-    launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAXERR, FQ>(in, s, amax, codes, scales, out, alpha_out, stream);
+    launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAXERR, FQ, DIAG>(
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stream);
   }
 }
 
@@ -581,7 +648,8 @@ hipError_t launch_alpha(const uint32_t* amax_bits, float* alpha, const Shape& s,
 // (out_alpha is the amax accumulator); otherwise the caller's amax.
 nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int block, int mode,
                  int rule, const float* amax_in, uint8_t* codes, uint8_t* scales, uint16_t* out,
-                 float* alpha, bool fq, hipStream_t stream) {
+                 float* alpha, bool fq, hipStream_t stream, uint8_t* qstar = nullptr,
+                 uint32_t* count4 = nullptr) {
   Shape s;
   nvfp4_status st = check_shape(E, rows, cols, &s);
   if (st != NVFP4_OK) return st;
@@ -610,18 +678,38 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
       return NVFP4_ERR_ALIAS;
   }
 
+  const bool diag = qstar != nullptr;
+  if (diag) {
+    if (!count4) return NVFP4_ERR_NULL;
+    if (!aligned(count4, 4)) return NVFP4_ERR_ALIGN;
+    const int64_t qb = s.E * s.nblk, in_bytes2 = s.E * s.n * 2;
+    if (overlap(qstar, qb, in, in_bytes2) || overlap(qstar, qb, codes, s.E * s.n / 2) ||
+        overlap(qstar, qb, scales, s.E * s.nblk) || overlap(qstar, qb, alpha, s.E * 4) ||
+        overlap(qstar, qb, count4, s.E * 4) || overlap(count4, s.E * 4, in, in_bytes2) ||
+        overlap(count4, s.E * 4, codes, s.E * s.n / 2) ||
+        overlap(count4, s.E * 4, scales, s.E * s.nblk) || overlap(count4, s.E * 4, alpha, s.E * 4))
+      return NVFP4_ERR_ALIAS;
+  }
+
   (void)hipGetLastError();   // clear a stale error so the status below is this call's
   const float* amax = amax_in;
   if (!amax) {
-    if (launch_amax(in, s, reinterpret_cast<uint32_t*>(alpha), stream) != hipSuccess)
+    if (launch_amax(in, s, reinterpret_cast<uint32_t*>(alpha), stream, count4) != hipSuccess)
       return NVFP4_ERR_HIP;
     amax = alpha;
   }
   // With a separate amax buffer the quantize kernel writes alpha itself (one launch);
   // when alpha doubles as the amax accumulator a follow-up kernel converts it in place.
   float* alpha_in_kernel = amax == alpha ? nullptr : alpha;
-  if (fq) launch_quantize<true>(mode, rule, in, s, amax, nullptr, nullptr, out, alpha_in_kernel, stream);
-  else    launch_quantize<false>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel, stream);
+  if (fq)
+    launch_quantize<true, false>(mode, rule, in, s, amax, nullptr, nullptr, out, alpha_in_kernel,
+                                 nullptr, nullptr, stream);
+  else if (diag)
+    launch_quantize<false, true>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
+                                 qstar, count4, stream);
+  else
+    launch_quantize<false, false>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
+                                  nullptr, nullptr, stream);
   if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
   if (!alpha_in_kernel &&
       launch_alpha(reinterpret_cast<const uint32_t*>(amax), alpha, s, mode, stream) != hipSuccess)
@@ -661,6 +749,27 @@ NVFP4_EXPORT nvfp4_status nvfp4_amax(const uint16_t* in, int64_t E, int64_t rows
              ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+NVFP4_EXPORT nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                                           const float* alpha, int64_t E, int64_t rows,
+                                           int64_t cols, uint16_t* out, hipStream_t stream) {
+  Shape s;
+  nvfp4_status st = check_shape(E, rows, cols, &s);
+  if (st != NVFP4_OK) return st;
+  if (!codes || !scales || !alpha || !out) return NVFP4_ERR_NULL;
+  if (!aligned(codes, 8) || !aligned(alpha, 4) || !aligned(out, 16)) return NVFP4_ERR_ALIGN;
+  const int64_t out_bytes = s.E * s.n * 2;
+  if (overlap(out, out_bytes, codes, s.E * s.n / 2) || overlap(out, out_bytes, scales, s.E * s.nblk) ||
+      overlap(out, out_bytes, alpha, s.E * 4))
+    return NVFP4_ERR_ALIAS;
+  (void)hipGetLastError();
+  const int64_t want = (s.nblk + kThreads - 1) / kThreads;
+  const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, NVFP4_BLOCK_WGS / s.E));
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kThreads), 0,
+                     stream, reinterpret_cast<const uint2*>(codes), scales, alpha, s.nblk,
+                     reinterpret_cast<uint4*>(out));
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 NVFP4_EXPORT nvfp4_status nvfp4_quantize(const uint16_t* in, int64_t rows, int64_t cols, int block,
                                          nvfp4_mode mode, nvfp4_rule rule, uint8_t* out_codes,
                                          uint8_t* out_scales, float* out_alpha, hipStream_t stream) {
@@ -690,6 +799,17 @@ NVFP4_EXPORT nvfp4_status nvfp4_fakequant_batched(const uint16_t* in, int64_t E,
                                                   float* out_alpha, hipStream_t stream) {
   return run(in, E, rows, cols, block, mode, rule, nullptr, nullptr, nullptr, out, out_alpha,
              true, stream);
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_quantize_diag(const uint16_t* in, int64_t E, int64_t rows,
+                                              int64_t cols, int block, nvfp4_mode mode,
+                                              nvfp4_rule rule, uint8_t* out_codes,
+                                              uint8_t* out_scales, float* out_alpha,
+                                              uint8_t* out_qstar, uint32_t* out_count4,
+                                              hipStream_t stream) {
+  if (!out_qstar || !out_count4) return NVFP4_ERR_NULL;
+  return run(in, E, rows, cols, block, mode, rule, nullptr, out_codes, out_scales, nullptr,
+             out_alpha, false, stream, out_qstar, out_count4);
 }
 
 NVFP4_EXPORT nvfp4_status nvfp4_quantize_from_amax(const uint16_t* in, int64_t E, int64_t rows,

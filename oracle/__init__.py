@@ -73,6 +73,8 @@ def lib():
         L.orc_quantize.restype = i32
         L.orc_quantize_blocks.argtypes = [P, i64, i64, i64, i32, i32, P, P, i64, P, P, P, P]
         L.orc_quantize_blocks.restype = i32
+        L.orc_dequantize.argtypes = [P, P, P, i64, i64, i64, P]
+        L.orc_dequantize.restype = i32
         L.orc_inexact_subtractions.restype = i64
         _lib = L
     return _lib
@@ -200,6 +202,20 @@ def quantize_blocks(x_bits: np.ndarray, alpha_: np.ndarray, ids: np.ndarray,
     if rc != 0:
         raise ValueError("oracle rejected arguments (rc=%d)" % rc)
     return dict(codes=codes, scales=scales, y=y, qstar=q)
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, alpha_: np.ndarray) -> np.ndarray:
+    """Packed NVFP4 -> bf16 bit patterns; codes [..., rows, cols/2], scales [..., rows,
+    cols/16], alpha [E]."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    al = np.ascontiguousarray(alpha_, dtype=np.float32)
+    E = c.shape[0] if c.ndim == 3 else 1
+    rows, cols = c.shape[-2], c.shape[-1] * 2
+    y = np.empty(c.shape[:-1] + (cols,), np.uint16)
+    if lib().orc_dequantize(_p(c), _p(s), _p(al), E, rows, cols, _p(y)) != 0:
+        raise ValueError("oracle rejected arguments")
+    return y
 
 
 def inexact_subtractions() -> int:

@@ -316,6 +316,32 @@ int orc_quantize_blocks(const uint16_t* in, int64_t E, int64_t rows, int64_t col
   return 0;
 }
 
+int orc_dequantize(const uint8_t* codes, const uint8_t* scales, const float* alpha, int64_t E,
+                   int64_t rows, int64_t cols, uint16_t* y) {
+  if (!codes || !scales || !alpha || !y || E <= 0 || rows <= 0 || cols <= 0 || cols % 16 != 0)
+    return -1;
+  const int64_t nb = rows * cols / 16;
+  for (int64_t t = 0; t < E; ++t) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const int64_t g = t * nb + b;
+      const uint8_t s = scales[g];
+      uint16_t* yb = y + g * 16;
+      if (std::isnan(alpha[t]) || (s & 0x7F) == 0x7F) {       // poisoned tensor or NaN scale
+        for (int i = 0; i < 16; ++i) yb[i] = 0x7FC0;
+        continue;
+      }
+      // the block's step, as in quantization: d = RN32(dec(s) * alpha)
+      const float d = float(e4m3_value(s)) * alpha[t];
+      for (int i = 0; i < 16; ++i) {
+        const int code = (codes[g * 8 + i / 2] >> (4 * (i & 1))) & 0xF;
+        const float mag = float(kE2M1Mag[code & 7]) * d;     // RN32(val * d)
+        yb[i] = bf16_rne((code & 8) ? -mag : mag);
+      }
+    }
+  }
+  return 0;
+}
+
 int64_t orc_inexact_subtractions(void) { return g_inexact.load(); }
 
 }  // extern "C"

@@ -80,6 +80,12 @@ int      orc_quantize_blocks(const uint16_t* in, int64_t E, int64_t rows, int64_
                              int64_t nsel, uint8_t* codes, uint8_t* scales, uint16_t* y,
                              uint8_t* qstar);
 
+/* Dequantize packed NVFP4 to bf16: y = RNbf16(val(code) * RN32(dec(scale) * alpha)), sign
+ * from the code.  A NaN alpha or a NaN scale byte (0x7F / 0xFF) gives 0x7FC0 for the block.
+ * codes [E][rows][cols/2], scales [E][rows][cols/16], alpha [E], y [E][rows][cols]. */
+int      orc_dequantize(const uint8_t* codes, const uint8_t* scales, const float* alpha,
+                        int64_t E, int64_t rows, int64_t cols, uint16_t* y);
+
 /* Count of error subtractions e = x - xhat that were not exact (expected 0). */
 int64_t  orc_inexact_subtractions(void);
 

@@ -41,7 +41,8 @@ def test_header_declares_the_entry_points():
     assert names == sorted(["nvfp4_abi_version", "nvfp4_status_str", "nvfp4_amax",
                             "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
                             "nvfp4_fakequant_batched", "nvfp4_quantize_from_amax",
-                            "nvfp4_fakequant_from_amax"])
+                            "nvfp4_fakequant_from_amax", "nvfp4_dequantize",
+                            "nvfp4_quantize_diag"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -111,6 +112,24 @@ def test_batched_amax_and_fixed_scale_validation(L):
     assert L.nvfp4_quantize_from_amax(A, 2, 4, 32, 16, 1, 0, D + 4, B, C, D, None) == EALIAS
     assert L.nvfp4_fakequant_from_amax(A, 1, 4, 32, 16, 1, 0, None, B, D, None) == ENULL
     assert L.nvfp4_fakequant_from_amax(A, 1, 4, 32, 16, 1, 9, D, B, D, None) == EENUM
+
+
+def test_dequantize_validation(L):
+    f = L.nvfp4_dequantize
+    assert f(None, C, D, 1, 4, 32, A, None) == ENULL
+    assert f(B, C, D, 1, 4, 30, A, None) == ESHAPE
+    assert f(B + 4, C, D, 1, 4, 32, A, None) == EALIGN
+    assert f(B, C, D, 1, 4, 32, A + 8, None) == EALIGN
+    assert f(B, C, D, 1, 4, 32, B + 16, None) == EALIAS      # output over the codes
+
+
+def test_diag_validation(L):
+    f = L.nvfp4_quantize_diag
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, None, D + 64, None) == ENULL
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, None, None) == ENULL
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 66, None) == EALIGN
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C, D + 64, None) == EALIAS       # qstar over scales
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, A + 8, None) == EALIAS  # count4 in input
 
 
 def test_python_binding_checks_inputs():

@@ -321,3 +321,73 @@ def test_full_size_workloads_sampled(nv, orc, name, mode, rule, fq):
             assert torch.equal(dq.view(torch.int16), y.view(torch.int16))
     del xg
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("name,shape", SMALL, ids=[s[0] for s in SMALL])
+def test_dequantize_equals_fakequant_and_oracle(nv, orc, name, shape):
+    x = W.bits(W.generate(name, shape))
+    xg = to_gpu(x)
+    for mode, rule in (("rtn6", "mse"), ("four_over_six", "mae")):
+        c, s, a = nv.quantize(xg, mode, rule)
+        y = nv.dequantize(c, s, a)
+        yf, _ = nv.fakequant(xg, mode, rule)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), yf.view(torch.int16))
+        ref = orc.dequantize(c.cpu().numpy(), s.cpu().numpy(), a.cpu().numpy())
+        assert np.array_equal(u16(y), ref)
+
+
+def test_dequantize_arbitrary_bytes(nv, orc):
+    """Every code and every scale byte (NaN 0x7F/0xFF and negative scales included), a
+    NaN alpha in one tensor of a batch."""
+    rng = np.random.default_rng(8)
+    E, rows, cols = 3, 20, 512
+    codes = rng.integers(0, 256, size=(E, rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(E, rows, cols // 16), dtype=np.uint8)
+    scales[0, 0, :] = np.arange(cols // 16, dtype=np.uint8)
+    alpha = np.array([2.0 ** -8, np.nan, 3.1e-5], np.float32)
+    y = nv.dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                      torch.from_numpy(alpha).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(y), orc.dequantize(codes, scales, alpha))
+
+
+def test_dequantize_full_size_weight(nv, orc):
+    xt = full_input("weight")
+    xg = xt.cuda()
+    c, s, a = nv.quantize(xg, "four_over_six", "mse")
+    y = nv.dequantize(c, s, a)
+    yf, _ = nv.fakequant(xg, "four_over_six", "mse")
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), yf.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- diagnostics
+@pytest.mark.parametrize("name,shape", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
+def test_diag_choice_and_count(nv, orc, name, shape, mode, rule):
+    x = W.bits(W.generate(name, shape))
+    c, s, a, q, n4 = nv.quantize_diag(to_gpu(x), mode, rule)
+    torch.cuda.synchronize()
+    ref = orc.quantize(x, mode, rule, want_y=False, want_qstar=True)
+    assert np.array_equal(c.cpu().numpy(), ref["codes"])
+    assert np.array_equal(s.cpu().numpy(), ref["scales"])
+    assert np.array_equal(q.cpu().numpy(), ref["qstar"])
+    E = x.shape[0] if x.ndim == 3 else 1
+    want = (ref["qstar"].reshape(E, -1) == 4).sum(axis=1)
+    assert np.array_equal(n4.cpu().numpy(), want)
+    if mode == "four_over_six":
+        assert want.sum() > 0
+
+
+def test_diag_poison_and_edges(nv, orc):
+    x = W.bits(W.generate("moe", (3, 16, 64))).copy()
+    x[2, 3, 5] = 0x7FC0
+    for name, xb in (("poison", x), ("subnormal", EDGE["subnormal"]), ("zeros", EDGE["zeros"])):
+        c, s, a, q, n4 = nv.quantize_diag(to_gpu(xb), "four_over_six", "mse")
+        torch.cuda.synchronize()
+        ref = orc.quantize(xb, "four_over_six", "mse", want_y=False, want_qstar=True)
+        assert np.array_equal(q.cpu().numpy(), ref["qstar"]), name
+        E = xb.shape[0] if xb.ndim == 3 else 1
+        assert np.array_equal(n4.cpu().numpy(), (ref["qstar"].reshape(E, -1) == 4).sum(axis=1)), name

@@ -461,3 +461,25 @@ def test_scale_four_candidate_is_capped_at_four_with_subnormal_scales(orc):
         bit += sum(1 for v in xf if d > 0 and v / d > 5)
         assert all(Fraction(float(h)) <= 4 * d * (1 + Fraction(1, 1 << 20)) for h in xh)
     assert bit > 0                    # the cap was exercised
+
+
+@pytest.mark.parametrize("name,shape", SMALL)
+@pytest.mark.parametrize("mode,rule", [("rtn6", "mse"), ("four_over_six", "mae")])
+def test_dequantize_of_packed_equals_fakequant(orc, name, shape, mode, rule):
+    """Decoding the packed output reproduces the simulated-quantization output."""
+    x = _small(name, shape)
+    r = orc.quantize(x, mode, rule)
+    assert np.array_equal(orc.dequantize(r["codes"], r["scales"], r["alpha"]), r["y"])
+
+
+def test_dequantize_closed_forms(orc):
+    # scale 0x38 = 1.0, alpha 2^-8: code 0x7 = 6 -> 6/256, code 0xE = -4 -> -4/256, 0x8 -> -0
+    codes = np.array([[0x87, 0x0E, 0, 0, 0, 0, 0, 0]], np.uint8)
+    y = orc.dequantize(codes, np.array([[0x38]], np.uint8), np.array([2.0 ** -8], np.float32))
+    want = bf16_bits([6 / 256, -0.0, -4 / 256, 0.0] + [0.0] * 12)
+    assert np.array_equal(y.ravel(), want)
+    # NaN scale byte and NaN alpha give NaN blocks
+    y = orc.dequantize(codes, np.array([[0x7F]], np.uint8), np.array([1.0], np.float32))
+    assert (y == 0x7FC0).all()
+    y = orc.dequantize(codes, np.array([[0x38]], np.uint8), np.array([np.nan], np.float32))
+    assert (y == 0x7FC0).all()
