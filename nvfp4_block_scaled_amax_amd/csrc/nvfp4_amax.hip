@@ -156,15 +156,6 @@ __global__ void alpha_kernel(const uint32_t* amax_bits, float* alpha,
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-#ifndef NVFP4_UNIT_BLOCKS
-#define NVFP4_UNIT_BLOCKS 1          // 16-element blocks owned by one lane per step
-#endif
-#ifndef NVFP4_PREFETCH
-#define NVFP4_PREFETCH 1             // grid-stride steps whose loads are in flight ahead
-#endif
-#ifndef NVFP4_SPLIT_CANDIDATES
-#define NVFP4_SPLIT_CANDIDATES 0
-#endif
 #ifndef NVFP4_WAVES_PER_EU
 #define NVFP4_WAVES_PER_EU 4         // occupancy floor: caps the block pass at 128 VGPRs
 #endif
@@ -342,12 +333,12 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
   s = s6;
   d = D6.x;
   if (MODE == NVFP4_FOUR_OVER_SIX) {
-#if NVFP4_SPLIT_CANDIDATES
-    __builtin_amdgcn_sched_barrier(0);   // keep the two trials apart: fewer live registers
-#endif
     const uint32_t s4 = (sp >> 8) & 0xFFu;
     const f32x2 D4 = tb.D[s4];
-    slow = slow || m * D4.y > 5.0f;
+    // Scaled values can pass 5 (so the cap at FP4 value 4 bites) only when the E4M3 scale
+    // rounded far down: a subnormal byte, or the clamp at 448.  A normal byte is within 1/16
+    // of sigma, so the block max lands at most near 4.27.
+    slow = slow || (s4 - 8u) >= 0x76u;
     uint32_t a4, b4;
     const float err4 = fast_candidate<RULE>(x, D4.y, D4.x, a4, b4);
     if (err4 < err6) { s = s4; d = D4.x; w0 = a4; w1 = b4; four = true; }   // ties keep 6
@@ -376,17 +367,18 @@ __device__ __forceinline__ void dequant_bf16(uint32_t w0, uint32_t w1, float d, 
 #undef NVFP4_DQ
 }
 
-// Grid: x = workgroups per tensor (grid-stride over units of K blocks), y = tensor.
-// Each lane owns K consecutive blocks per step; the next step's loads are issued before
-// the current step's arithmetic.  DIAG (packed output only) also writes, per block, the
-// block maximum it was scaled to (4 or 6) and counts the blocks scaled to 4 per tensor.
+// Grid: x = workgroups per tensor, y = tensor.  Lane = one 16-element block per step,
+// grid-stride over the tensor's blocks; the next step's two 16-byte loads are issued before
+// the current step's arithmetic.  Block indices are 32-bit (the host splits tensors of 2^27
+// blocks or more into launches below that), so every access is a uniform 64-bit base plus a
+// 32-bit lane offset.  DIAG (packed output only) also writes, per block, the block maximum
+// it was scaled to (4 or 6) and counts the blocks scaled to 4 per tensor.
 template <int MODE, int RULE, bool FQ, bool DIAG>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     const uint4* __restrict__ in, int64_t nblk, const float* __restrict__ amax,
     uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
     float* __restrict__ alpha_out, uint8_t* __restrict__ qstar, uint32_t* __restrict__ count4) {
-  constexpr int K = NVFP4_UNIT_BLOCKS;
   __shared__ BlockTables tb;
   const int64_t t = blockIdx.y;
   const uint32_t abits = __float_as_uint(amax[t]) & 0x7FFFFFFFu;
@@ -397,27 +389,26 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   if (alpha_out && blockIdx.x == 0 && threadIdx.x == 0)
     alpha_out[t] = poison ? __uint_as_float(0x7FC00000u) : alpha;
 
-  const int64_t nunits = (nblk + K - 1) / K;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  const int64_t base = t * nblk;                 // first block of this tensor
-  int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // this tensor's arrays (uniform) and 32-bit block indices
+  const int64_t base = t * nblk;
+  const char* inT = reinterpret_cast<const char*>(in + 2 * base);       // 32 bytes per block
+  char* codesT = reinterpret_cast<char*>(codes + base);                  // 8 bytes per block
+  uint8_t* scalesT = scales + base;
+  char* outT = reinterpret_cast<char*>(out + 2 * base);                  // 32 bytes per block
+  const uint32_t n = (uint32_t)nblk;
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t u = blockIdx.x * kThreads + threadIdx.x;
 
   if (poison) {                                  // non-finite input or amax
-    for (; u < nunits; u += stride) {
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int64_t b = u * K + k;
-        if (b < nblk) {
-          if (FQ) {
-            const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-            out[2 * (base + b)] = nan4;
-            out[2 * (base + b) + 1] = nan4;
-          } else {
-            codes[base + b] = make_uint2(0u, 0u);
-            scales[base + b] = 0x7F;
-            if (DIAG) qstar[base + b] = 0;
-          }
-        }
+    for (; u < n; u += stride) {
+      if (FQ) {
+        const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+        *reinterpret_cast<uint4*>(outT + (u << 5)) = nan4;
+        *reinterpret_cast<uint4*>(outT + (u << 5) + 16) = nan4;
+      } else {
+        *reinterpret_cast<uint2*>(codesT + (u << 3)) = make_uint2(0u, 0u);
+        scalesT[u] = 0x7F;
+        if (DIAG) qstar[base + u] = 0;
       }
     }
     return;
@@ -429,79 +420,43 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   __syncthreads();
   const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
 
-  constexpr int PF = NVFP4_PREFETCH;            // units in flight ahead of the one computed
-  uint4 ring[PF][2 * K];
-  auto load_unit = [&](uint4 (&dst)[2 * K], int64_t uu) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int64_t b = uu * K + k;
-      if (K == 1 || b < nblk) {
-        dst[2 * k] = in[2 * (base + b)];
-        dst[2 * k + 1] = in[2 * (base + b) + 1];
-      } else {
-        dst[2 * k] = make_uint4(0u, 0u, 0u, 0u);
-        dst[2 * k + 1] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-#pragma unroll
-  for (int f = 0; f < PF; ++f)
-    if (u + f * stride < nunits) load_unit(ring[f], u + f * stride);
-  for (; u < nunits; u += stride) {
-    uint4 cur[2 * K];
-#pragma unroll
-    for (int k = 0; k < 2 * K; ++k) cur[k] = ring[0][k];
-#pragma unroll
-    for (int f = 0; f + 1 < PF; ++f)
-#pragma unroll
-      for (int k = 0; k < 2 * K; ++k) ring[f][k] = ring[f + 1][k];
-    if (K == 1)          // always in bounds: past the end it reloads the last unit
-      load_unit(ring[PF - 1], min(u + PF * stride, nunits - 1));
-    else if (u + PF * stride < nunits)
-      load_unit(ring[PF - 1], u + PF * stride);
+  uint4 nx0 = make_uint4(0u, 0u, 0u, 0u), nx1 = nx0;
+  if (u < n) {
+    nx0 = *reinterpret_cast<const uint4*>(inT + (u << 5));
+    nx1 = *reinterpret_cast<const uint4*>(inT + (u << 5) + 16);
+  }
+  for (; u < n; u += stride) {
+    const uint4 c0 = nx0, c1 = nx1;
+    const uint32_t un = min(u + stride, n - 1);   // always in bounds: reloads the last block
+    nx0 = *reinterpret_cast<const uint4*>(inT + (un << 5));
+    nx1 = *reinterpret_cast<const uint4*>(inT + (un << 5) + 16);
 
-    uint32_t sc[K], w0[K], w1[K];
-    float dq[K], bm[K];
-    bool slow[K], four[K];
-    bool any_slow = false;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      float x[16];
-      unpack16(cur[2 * k], cur[2 * k + 1], x);
-      fast_block<MODE, RULE>(x, tb, n6, n4, slow[k], sc[k], dq[k], w0[k], w1[k], bm[k], four[k]);
-      slow[k] = slow[k] || tiny_alpha;
-      any_slow = any_slow || slow[k];
+    float x[16];
+    unpack16(c0, c1, x);
+    uint32_t sc, w0, w1;
+    float dq, bm;
+    bool slow, four;
+    fast_block<MODE, RULE>(x, tb, n6, n4, slow, sc, dq, w0, w1, bm, four);
+    if (slow || tiny_alpha) {        // rare: redo the block on the reference path
+      const RefOut o =
+          ref_block<MODE, RULE>(reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm, alpha);
+      sc = o.s;
+      dq = o.d;
+      w0 = o.w0;
+      w1 = o.w1;
+      four = o.four;
     }
-    if (any_slow) {                  // rare: redo those blocks on the reference path
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        if (slow[k]) {
-          const RefOut o = ref_block<MODE, RULE>(
-              reinterpret_cast<const uint16_t*>(in + 2 * (base + u * K + k)), bm[k], alpha);
-          sc[k] = o.s;
-          dq[k] = o.d;
-          w0[k] = o.w0;
-          w1[k] = o.w1;
-          four[k] = o.four;
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int64_t b = u * K + k;
-      if (K > 1 && b >= nblk) break;
-      if (FQ) {
-        uint32_t y[8];
-        dequant_bf16(w0[k], w1[k], dq[k], y);
-        out[2 * (base + b)] = make_uint4(y[0], y[1], y[2], y[3]);
-        out[2 * (base + b) + 1] = make_uint4(y[4], y[5], y[6], y[7]);
-      } else {
-        codes[base + b] = make_uint2(w0[k], w1[k]);
-        scales[base + b] = (uint8_t)sc[k];
-        if (DIAG) {
-          qstar[base + b] = four[k] ? 4 : 6;
-          n_four += four[k] ? 1u : 0u;
-        }
+    if (FQ) {
+      uint32_t y[8];
+      dequant_bf16(w0, w1, dq, y);
+      *reinterpret_cast<uint4*>(outT + (u << 5)) = make_uint4(y[0], y[1], y[2], y[3]);
+      *reinterpret_cast<uint4*>(outT + (u << 5) + 16) = make_uint4(y[4], y[5], y[6], y[7]);
+    } else {
+      *reinterpret_cast<uint2*>(codesT + (u << 3)) = make_uint2(w0, w1);
+      scalesT[u] = (uint8_t)sc;
+      if (DIAG) {
+        qstar[base + u] = four ? 4 : 6;
+        n_four += four ? 1u : 0u;
       }
     }
   }
@@ -602,19 +557,32 @@ hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStr
   return hipGetLastError();
 }
 
+constexpr int64_t kMaxLaunchBlocks = (INT64_C(1) << 27) - 1;   // 32-bit byte offsets in kernels
+
 template <int MODE, int RULE, bool FQ, bool DIAG>
 void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, uint8_t* codes,
                        uint8_t* scales, uint16_t* out, float* alpha_out, uint8_t* qstar,
                        uint32_t* count4, hipStream_t stream) {
-  const int64_t units = (s.nblk + NVFP4_UNIT_BLOCKS - 1) / NVFP4_UNIT_BLOCKS;
-  const int64_t want = (units + kThreads - 1) / kThreads;
-  const int64_t per_tensor =
-      std::max<int64_t>(1, std::min<int64_t>(want, NVFP4_BLOCK_WGS / s.E));
-  const dim3 grid((unsigned)per_tensor, (unsigned)s.E);
-  hipLaunchKernelGGL((quantize_kernel<MODE, RULE, FQ, DIAG>), grid, dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(in), s.nblk, amax,
-                     reinterpret_cast<uint2*>(codes), scales, reinterpret_cast<uint4*>(out),
-                     alpha_out, qstar, count4);
+  auto launch = [&](int64_t E, int64_t nblk, int64_t first_tensor, int64_t first_block) {
+    const int64_t want = (nblk + kThreads - 1) / kThreads;
+    const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, NVFP4_BLOCK_WGS / E));
+    const int64_t b0 = first_tensor * s.nblk + first_block;   // first block of this launch
+    hipLaunchKernelGGL((quantize_kernel<MODE, RULE, FQ, DIAG>),
+                       dim3((unsigned)per_tensor, (unsigned)E), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const uint4*>(in + b0 * 16), nblk, amax + first_tensor,
+                       reinterpret_cast<uint2*>(codes ? codes + b0 * 8 : nullptr),
+                       scales ? scales + b0 : nullptr,
+                       reinterpret_cast<uint4*>(out ? out + b0 * 16 : nullptr),
+                       alpha_out ? alpha_out + first_tensor : nullptr, qstar ? qstar + b0 : nullptr,
+                       count4 ? count4 + first_tensor : nullptr);
+  };
+  if (s.nblk <= kMaxLaunchBlocks) {
+    launch(s.E, s.nblk, 0, 0);
+  } else {                  // tensors of 2^27 blocks or more: one launch per tensor and chunk
+    for (int64_t t = 0; t < s.E; ++t)
+      for (int64_t b = 0; b < s.nblk; b += kMaxLaunchBlocks)
+        launch(1, std::min(kMaxLaunchBlocks, s.nblk - b), t, b);
+  }
 }
 
 template <bool FQ, bool DIAG>
