@@ -110,15 +110,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Grid: x = workgroups per tensor, y = tensor.  Few, large workgroups (one atomic each:
 // same-address atomics serialize, so their count is kept near the CU count).  Each lane
-// reads 8 consecutive 16-byte chunks (128 bytes, 64 bf16 values) per step, the workgroups
-// striding over the tensor.
+// reads C consecutive 16-byte chunks per step, the workgroups striding over the tensor:
+// C = 8 (128 bytes, 64 bf16 values) when that still gives every tensor its share of the
+// workgroups, else C = 1 so that small tensors spread over more CUs.
 constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxWGs = 256;
-constexpr int kAmaxChunks = 8;
+template <int C>
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restrict__ in,
                                                             int64_t chunks,
                                                             uint32_t* __restrict__ acc) {
-  constexpr int C = kAmaxChunks;
   const uint4* p = in + (int64_t)blockIdx.y * chunks;
   const int64_t stride = (int64_t)gridDim.x * kAmaxThreads * C;
   int64_t i = ((int64_t)blockIdx.x * kAmaxThreads + threadIdx.x) * C;
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restr
 #pragma unroll
     for (int k = 0; k < C; ++k) m = mag_max8(m, v[k]);
   }
-  for (; i < chunks; ++i) m = mag_max8(m, p[i]);   // the one lane whose chunks run past the end
+  if (C > 1)
+    for (; i < chunks; ++i) m = mag_max8(m, p[i]);   // the one lane whose chunks run past the end
   // the larger of the two 16-bit magnitudes, as the bits of a binary32 value
   m = max(m & 0xFFFFu, m >> 16) << 16;
   m = wave_max_u32(m);
@@ -160,8 +161,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #define NVFP4_WAVES_PER_EU 4         // occupancy floor: caps the block pass at 128 VGPRs
 #endif
 #ifndef NVFP4_BLOCK_WGS
-#define NVFP4_BLOCK_WGS 1024         // target workgroups of the block pass (all tensors)
+#define NVFP4_BLOCK_WGS 1024        // workgroups of the block pass over all tensors of a launch
 #endif
+// Launches of at least 2^23 blocks (268 MB of bf16 input and more) run on three 256-thread
+// workgroups per CU instead of four: measured 2-3 % faster than four on 470 MB and 1.3 GB
+// inputs, and 3-5 % slower on 67-117 MB inputs.
+#ifndef NVFP4_BLOCK_WGS_LONG
+#define NVFP4_BLOCK_WGS_LONG 768
+#endif
+constexpr int64_t kLongLaunchBlocks = INT64_C(1) << 23;
 
 // Reference path for one candidate, straight from the definition, one binary32 step at a
 // time (correctly rounded division and reciprocal, threshold-count FP4 rounding).  The
@@ -548,12 +556,19 @@ nvfp4_status check_common(const uint16_t* in, const Shape& s, int block, int mod
 hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStream_t stream,
                        uint32_t* acc2 = nullptr) {
   const int64_t chunks = s.n / 8;
-  const int64_t want = (chunks + kAmaxThreads * kAmaxChunks - 1) / (kAmaxThreads * kAmaxChunks);
-  const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, kAmaxWGs / s.E));
+  const int64_t share = std::max<int64_t>(1, kAmaxWGs / s.E);   // workgroups per tensor
+  const int64_t want8 = (chunks + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
+  const int64_t want1 = (chunks + kAmaxThreads - 1) / kAmaxThreads;
+  const bool wide = want8 >= share;
+  const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(wide ? want8 : want1, share));
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((s.E + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                      stream, acc, acc2, s.E);
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads), 0,
-                     stream, reinterpret_cast<const uint4*>(in), chunks, acc);
+  if (wide)
+    hipLaunchKernelGGL(amax_kernel<8>, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
+                       0, stream, reinterpret_cast<const uint4*>(in), chunks, acc);
+  else
+    hipLaunchKernelGGL(amax_kernel<1>, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
+                       0, stream, reinterpret_cast<const uint4*>(in), chunks, acc);
   return hipGetLastError();
 }
 
@@ -565,7 +580,8 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
                        uint32_t* count4, hipStream_t stream) {
   auto launch = [&](int64_t E, int64_t nblk, int64_t first_tensor, int64_t first_block) {
     const int64_t want = (nblk + kThreads - 1) / kThreads;
-    const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, NVFP4_BLOCK_WGS / E));
+    const int64_t wgs = E * nblk >= kLongLaunchBlocks ? NVFP4_BLOCK_WGS_LONG : NVFP4_BLOCK_WGS;
+    const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, wgs / E));
     const int64_t b0 = first_tensor * s.nblk + first_block;   // first block of this launch
     hipLaunchKernelGGL((quantize_kernel<MODE, RULE, FQ, DIAG>),
                        dim3((unsigned)per_tensor, (unsigned)E), dim3(kThreads), 0, stream,

@@ -171,6 +171,28 @@ def test_amax_matches_oracle(nv, orc):
         assert np.array_equal(got.view(np.uint32), orc.amax(x, E).view(np.uint32)), name
 
 
+# Both amax variants (8 chunks per lane step for tensors that fill their workgroups, 1 chunk
+# otherwise), tensors whose chunk count is not a multiple of 8 (the 8-chunk variant's tail
+# lane), and the maximum planted first, last and in the middle of each tensor.
+AMAX_SHAPES = [(1, 16), (7, 48), (2049, 8208), (3, 1000, 5136), (3, 1001, 5648), (300, 2, 32)]
+
+
+@pytest.mark.parametrize("shape", AMAX_SHAPES, ids=["x".join(map(str, s)) for s in AMAX_SHAPES])
+def test_amax_variants_and_tails(nv, orc, shape):
+    E = shape[0] if len(shape) == 3 else 1
+    base = W.bits(W.generate("weight", shape)).reshape(E, -1)
+    big = bf16_bits(np.array([3.0, -5.5, 7.25], np.float32))
+    for where in ("first", "last", "middle"):
+        x = base.copy()
+        for t in range(E):
+            pos = {"first": 0, "last": x.shape[1] - 1, "middle": x.shape[1] // 2 + 3}[where]
+            x[t, pos] = big[t % 3]
+        x = x.reshape(shape)
+        say("amax %s max %s" % (shape, where))
+        got = nv.amax(to_gpu(x)).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), orc.amax(x, E).view(np.uint32)), (shape, where)
+
+
 @pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
 def test_fixed_scale_entry(nv, orc, mode, rule):
     x = W.bits(W.generate("moe", (3, 40, 160)))
