@@ -75,6 +75,8 @@ def lib():
         L.orc_quantize_blocks.restype = i32
         L.orc_dequantize.argtypes = [P, P, P, i64, i64, i64, P]
         L.orc_dequantize.restype = i32
+        L.orc_quantize_stats.argtypes = [P, i64, i64, i64, i32, i32, P, i32]
+        L.orc_quantize_stats.restype = i32
         L.orc_inexact_subtractions.restype = i64
         _lib = L
     return _lib
@@ -216,6 +218,27 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, alpha_: np.ndarray) -> np.
     if lib().orc_dequantize(_p(c), _p(s), _p(al), E, rows, cols, _p(y)) != 0:
         raise ValueError("oracle rejected arguments")
     return y
+
+
+# Columns of quantize_stats (same order as the oracle's ORC_STAT_* constants).
+STATS = ("sse", "sae", "maxerr", "sse_near", "sse_f32scale", "near_count")
+
+
+def quantize_stats(x_bits: np.ndarray, mode="four_over_six", rule="mse",
+                   nthreads: int = 1) -> np.ndarray:
+    """Per-tensor error statistics of the quantization -> float64 [E, 6], columns STATS:
+    sum e^2, sum |e|, max |e|, sum e^2 over elements above 2/3 of their block max, sum e^2
+    with binary32 block scales instead of E4M3, and the count of elements above 2/3 of
+    their block max.  NaN rows for poisoned tensors."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    E = x.shape[0] if x.ndim == 3 else 1
+    rows, cols = x.shape[-2], x.shape[-1]
+    out = np.empty((E, len(STATS)), np.float64)
+    rc = lib().orc_quantize_stats(_p(x), E, rows, cols, _mode(mode), _rule(rule), _p(out),
+                                  int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected arguments (rc=%d)" % rc)
+    return out
 
 
 def inexact_subtractions() -> int:

@@ -106,13 +106,16 @@ struct Candidate {
 // its max maps to Q, round every value to FP4, dequantize, and measure the error against
 // the original values [4/6, "Adaptive block scaling algorithm": quantize twice, compute
 // both errors against the original high-precision values].
-void run_candidate(const float x[16], float bmax, float alpha, int Q, int rule, Candidate* c) {
+// e4m3_scale = false is a diagnostic only: the block scale sigma stays in binary32 instead
+// of being rounded to E4M3 (scale byte reported as 0), everything else unchanged.
+void run_candidate(const float x[16], float bmax, float alpha, int Q, int rule, Candidate* c,
+                   bool e4m3_scale = true) {
   // reading: block scale sigma = bmax / RN32(Q*alpha), then E4M3 (RNE, saturating).
   const float cq = float(Q) * alpha;
   const float sigma = alpha == 0.0f ? 0.0f : bmax / cq;
-  c->scale = uint8_t(e4m3_encode(sigma));
+  c->scale = e4m3_scale ? uint8_t(e4m3_encode(sigma)) : uint8_t(0);
   // reading: the block's dequantization step d = RN32(dec(s) * alpha).
-  const float d = float(e4m3_value(c->scale)) * alpha;
+  const float d = e4m3_scale ? float(e4m3_value(c->scale)) * alpha : sigma * alpha;
   // A block scaled to 4 lives in [-4, 4] and gives up 5 and 6 [4/6, "core mechanism"]:
   // its magnitude code is capped at 4 (code 6).  Scale 6 keeps the full grid (code 7).
   const int cap = Q == 4 ? 6 : 7;
@@ -146,7 +149,8 @@ void run_candidate(const float x[16], float bmax, float alpha, int Q, int rule, 
 }
 
 void quantize_block(const float x[16], float alpha, int mode, int rule, uint8_t codes8[8],
-                    uint8_t* scale, uint16_t y16[16], orc_block_debug* dbg) {
+                    uint8_t* scale, uint16_t y16[16], orc_block_debug* dbg,
+                    Candidate* chosen = nullptr) {
   if (std::isnan(alpha)) {                        // poisoned tensor (non-finite input)
     std::memset(codes8, 0, 8);
     *scale = 0x7F;
@@ -175,12 +179,55 @@ void quantize_block(const float x[16], float alpha, int mode, int rule, uint8_t 
   }
   // simulated quantization output: the dequantized value rounded to bf16
   if (y16) for (int i = 0; i < 16; ++i) y16[i] = bf16_rne(win->xhat[i]);
+  if (chosen) *chosen = *win;
   if (dbg) {
     dbg->qstar = win == &c4 ? 4 : 6;
     dbg->s6 = c6.scale;
     dbg->err6 = c6.err;
     dbg->s4 = mode == ORC_FOUR_OVER_SIX ? c4.scale : 0;
     dbg->err4 = mode == ORC_FOUR_OVER_SIX ? c4.err : NAN;
+  }
+}
+
+// Error statistics of a quantized tensor (diagnostics; the encoding does not use them).
+// The Four Over Six explainer ("Problem definition") reports that, on a real model, the
+// error of rounding the block scales to FP8 matters little while rounding the values near
+// the block max (66.6 % to 100 % of it, where scale 6 has no FP4 value between 4 and 6)
+// drives the loss.  reading: per tensor, over the chosen candidate of every block,
+//   sse      = sum e_i^2           sae = sum |e_i|          maxerr = max |e_i|
+//   sse_near = sum e_i^2 over elements with |x_i| > (2/3) bmax of their block, near = their
+//              count (3|x| > 2 bmax, an exact comparison)
+//   sse_f32  = sum e_i^2 when the chosen candidate keeps its binary32 block scale sigma
+//              instead of the E4M3 byte (so sse - sse_f32 is what rounding the scales costs)
+// e_i = x_i - xhat_i is exact (binary32), so each term e_i^2 is exact in long double; the
+// sums are taken in long double in element order.
+struct TensorStats {
+  long double sse = 0, sae = 0, sse_near = 0, sse_f32 = 0;
+  float maxerr = 0.0f;
+  int64_t near = 0;
+};
+
+void accumulate_block_stats(const float x[16], float alpha, int mode, int rule,
+                            TensorStats* st) {
+  uint8_t codes8[8], scale;
+  orc_block_debug dbg;
+  Candidate win, f32;
+  quantize_block(x, alpha, mode, rule, codes8, &scale, nullptr, &dbg, &win);
+  float bmax = 0.0f;
+  for (int i = 0; i < 16; ++i) bmax = std::max(bmax, std::fabs(x[i]));
+  run_candidate(x, bmax, alpha, dbg.qstar, rule, &f32, /*e4m3_scale=*/false);
+  for (int i = 0; i < 16; ++i) {
+    const float e = x[i] - win.xhat[i];
+    const long double e2 = (long double)e * (long double)e;
+    st->sse += e2;
+    st->sae += std::fabs((long double)e);
+    st->maxerr = std::max(st->maxerr, std::fabs(e));
+    if (3.0 * std::fabs(double(x[i])) > 2.0 * double(bmax)) {
+      st->sse_near += e2;
+      ++st->near;
+    }
+    const float eu = x[i] - f32.xhat[i];
+    st->sse_f32 += (long double)eu * (long double)eu;
   }
 }
 
@@ -338,6 +385,50 @@ int orc_dequantize(const uint8_t* codes, const uint8_t* scales, const float* alp
         yb[i] = bf16_rne((code & 8) ? -mag : mag);
       }
     }
+  }
+  return 0;
+}
+
+int orc_quantize_stats(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int mode,
+                       int rule, double* stats, int nthreads) {
+  if (bad_args(in, E, rows, cols, mode, rule) || !stats) return -1;
+  const int64_t n = rows * cols, nb = n / 16;
+  const int nt = std::max(1, nthreads);
+  for (int64_t t = 0; t < E; ++t) {
+    const uint16_t* x = in + t * n;
+    double* out = stats + t * ORC_NSTATS;
+    const float amax = tensor_amax(x, n);
+    if (std::isnan(amax)) {                       // poisoned tensor: no statistics
+      for (int k = 0; k < ORC_NSTATS; ++k) out[k] = NAN;
+      continue;
+    }
+    const float al = alpha_of(amax, mode);
+    // contiguous block ranges, combined in range order
+    const int64_t chunk = (nb + nt - 1) / nt;
+    std::vector<TensorStats> parts(nt);
+    parallel_ranges(nb, nt, [&](int64_t lo, int64_t hi) {
+      TensorStats& p = parts[lo / std::max<int64_t>(1, chunk)];
+      for (int64_t b = lo; b < hi; ++b) {
+        float xb[16];
+        for (int i = 0; i < 16; ++i) xb[i] = bf16_value(x[b * 16 + i]);
+        accumulate_block_stats(xb, al, mode, rule, &p);
+      }
+    });
+    TensorStats tot;
+    for (const TensorStats& p : parts) {
+      tot.sse += p.sse;
+      tot.sae += p.sae;
+      tot.sse_near += p.sse_near;
+      tot.sse_f32 += p.sse_f32;
+      tot.maxerr = std::max(tot.maxerr, p.maxerr);
+      tot.near += p.near;
+    }
+    out[ORC_STAT_SSE] = double(tot.sse);
+    out[ORC_STAT_SAE] = double(tot.sae);
+    out[ORC_STAT_MAXERR] = double(tot.maxerr);
+    out[ORC_STAT_SSE_NEAR] = double(tot.sse_near);
+    out[ORC_STAT_SSE_F32SCALE] = double(tot.sse_f32);
+    out[ORC_STAT_NEAR_COUNT] = double(tot.near);
   }
   return 0;
 }

@@ -86,6 +86,16 @@ int      orc_quantize_blocks(const uint16_t* in, int64_t E, int64_t rows, int64_
 int      orc_dequantize(const uint8_t* codes, const uint8_t* scales, const float* alpha,
                         int64_t E, int64_t rows, int64_t cols, uint16_t* y);
 
+/* Error statistics per tensor (diagnostics), stats [E][ORC_NSTATS] as double, over the
+ * chosen candidate of every block: sum e^2, sum |e|, max |e|, sum e^2 over the elements
+ * above two thirds of their block max, the same sum with each block's binary32 scale
+ * instead of its E4M3 byte, and the count of elements above two thirds of their block
+ * max.  Sums in long double, element order.  A poisoned tensor gets NaN everywhere. */
+enum { ORC_STAT_SSE = 0, ORC_STAT_SAE = 1, ORC_STAT_MAXERR = 2, ORC_STAT_SSE_NEAR = 3,
+       ORC_STAT_SSE_F32SCALE = 4, ORC_STAT_NEAR_COUNT = 5, ORC_NSTATS = 6 };
+int      orc_quantize_stats(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
+                            int mode, int rule, double* stats, int nthreads);
+
 /* Count of error subtractions e = x - xhat that were not exact (expected 0). */
 int64_t  orc_inexact_subtractions(void);
 

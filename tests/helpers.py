@@ -53,6 +53,8 @@ def read_examples(name: str = "worked_examples.txt"):
                 cur[key] = [int(v, 16) for v in vals]
             elif key == "qstar":
                 cur[key] = [int(v) for v in vals]
+            elif key == "stats":
+                cur[key] = [2.0 ** int(v[2:]) if v.startswith("2^") else float(v) for v in vals]
             else:
                 raise ValueError("unknown key %r in %s" % (key, name))
     return out

@@ -167,6 +167,7 @@ def test_worked_example(orc, ex):
         assert np.array_equal(r["y"].ravel(), bf16_bits(ex["y"])), rule
         q = orc.quantize(x, ex["mode"], rule, want_qstar=True)["qstar"]
         assert list(q.ravel()) == ex["qstar"], rule
+        assert list(orc.quantize_stats(x, ex["mode"], rule)[0]) == ex["stats"], rule
 
 
 def test_page_fact_four_is_two_thirds_of_the_max_under_scale_six(orc):
@@ -483,3 +484,117 @@ def test_dequantize_closed_forms(orc):
     assert (y == 0x7FC0).all()
     y = orc.dequantize(codes, np.array([[0x38]], np.uint8), np.array([np.nan], np.float32))
     assert (y == 0x7FC0).all()
+
+
+# ----------------------------------------------------------------------------- error statistics
+# Columns: sum e^2, sum |e|, max |e|, sum e^2 over |x| > 2/3 bmax, sum e^2 with binary32
+# block scales, count of |x| > 2/3 bmax.
+SSE, SAE, MAXERR, SSE_NEAR, SSE_F32, NEAR = range(6)
+
+
+def test_stats_near_max_band_is_strictly_above_two_thirds(orc):
+    # [6, 4, 3, 5, 0...] under rtn6 with amax 6: 4 is exactly 2/3 of the block max, so only
+    # 6 and 5 are in the band the pages single out (66.6 % to 100 % of the block max).
+    x = bf16_bits([6.0, 4.0, 3.0, 5.0] + [0.0] * 12).reshape(1, 16)
+    st = orc.quantize_stats(x, "rtn6", "mse")[0]
+    assert st[NEAR] == 2
+    # alpha = 6/2688, sigma = RN32(6 / RN32(6 alpha)) rounds to 448; the 5 is the only
+    # value that the step cannot hit, so it carries the near-band error alone
+    r = orc.quantize(x, "rtn6", "mse")
+    xhat = bf16_to_f32(r["y"]).ravel()
+    assert st[SSE_NEAR] > 0 and st[SSE_NEAR] <= st[SSE]
+    assert xhat[1] == 4.0 and xhat[2] == 3.0
+
+
+def _exact_stats(orc, x_bits, mode, rule):
+    """Brute force in exact rationals from the encoded output: xhat from the codes and
+    scale bytes, e = x - xhat exactly, the near band by an exact comparison, and the
+    binary32-scale trial recomputed from the IEEE definition with a brute-force nearest
+    FP4 value (ties to the even code, capped at 4 for blocks scaled to 4)."""
+    r = orc.quantize(x_bits, mode, rule, want_qstar=True)
+    al = Fraction(float(r["alpha"][0]))
+    xs = bf16_to_f32(x_bits).reshape(-1, 16)
+    codes = r["codes"].reshape(-1, 8)
+    sse = sae = near_sse = f32_sse = Fraction(0)
+    mx, near = Fraction(0), 0
+    for b in range(xs.shape[0]):
+        xf = [Fraction(float(v)) for v in xs[b]]
+        bmax = max(abs(v) for v in xf)
+        d = _rn32(Fraction(orc.e4m3_decode(int(r["scales"].ravel()[b]))) * al)
+        Q = int(r["qstar"].ravel()[b])
+        cq = _rn32(Q * al)
+        sig = _rn32(bmax / cq) if al != 0 else Fraction(0)
+        du = _rn32(sig * al)
+        ru = _rn32(1 / du) if du != 0 else Fraction(0)
+        for i, xv in enumerate(xf):
+            c = (int(codes[b, i // 2]) >> (4 * (i % 2))) & 15
+            xh = _rn32(Fraction(GRID[c & 7]) * d)
+            e = abs(xv) - xh                      # xhat carries the sign of x
+            sse += e * e
+            sae += abs(e)
+            mx = max(mx, abs(e))
+            if 3 * abs(xv) > 2 * bmax:
+                near_sse += e * e
+                near += 1
+            m = 0
+            if du != 0:
+                v = abs(_rn32(xv * ru))
+                m = _nearest_code_exact(v, Fraction(1), 6 if Q == 4 else 7)
+            eu = _rn32(abs(xv) - _rn32(Fraction(GRID[m]) * du))
+            f32_sse += eu * eu
+    return [sse, sae, mx, near_sse, f32_sse, Fraction(near)]
+
+
+def test_stats_equal_exact_sums_on_tiny_tensors(orc):
+    """Every statistic against exact rational arithmetic: the maximum and the count
+    exactly, the sums within one rounding to binary64 plus the long-double accumulation
+    (relative 2^-51 at these sizes)."""
+    tol = Fraction(1, 1 << 51)
+    for seed, (mode, rule) in enumerate([("rtn6", "mse"), ("four_over_six", "mse"),
+                                         ("four_over_six", "mae"), ("four_over_six", "maxerr")]):
+        blocks = _random_blocks(48, 60 + seed)
+        x = blocks.reshape(1, -1)
+        got = orc.quantize_stats(x, mode, rule)[0]
+        exact = _exact_stats(orc, x, mode, rule)
+        for k in (SSE, SAE, SSE_NEAR, SSE_F32):
+            assert abs(Fraction(float(got[k])) - exact[k]) <= tol * exact[k], (mode, rule, k)
+        assert Fraction(float(got[MAXERR])) == exact[MAXERR]
+        assert got[NEAR] == exact[NEAR]
+        assert exact[SSE_F32] != exact[SSE]       # the scale rounding shows in the data
+
+
+@pytest.mark.parametrize("name,shape", SMALL)
+@pytest.mark.parametrize("mode,rule", [("rtn6", "mse"), ("four_over_six", "mse"),
+                                       ("four_over_six", "mae")])
+def test_stats_invariants(orc, name, shape, mode, rule):
+    x = _small(name, shape)
+    E = x.shape[0] if x.ndim == 3 else 1
+    st = orc.quantize_stats(x, mode, rule)
+    n = x.size // E
+    xb = np.abs(bf16_to_f32(x)).reshape(E, -1, 16)
+    nonzero_blocks = (xb.max(axis=2) > 0).sum(axis=1)
+    for t in range(E):
+        s_ = st[t]
+        assert 0 <= s_[SSE_NEAR] <= s_[SSE]
+        assert s_[MAXERR] ** 2 <= s_[SSE] * (1 + 1e-12) and s_[SSE] <= n * s_[MAXERR] ** 2
+        assert s_[SAE] ** 2 <= n * s_[SSE] * (1 + 1e-12) and s_[SAE] <= n * s_[MAXERR]
+        assert nonzero_blocks[t] <= s_[NEAR] <= n        # every block max is in its band
+        assert s_[SSE_F32] > 0
+    # scaling by 2^k scales the sums exactly (no rounding depends on the exponent here)
+    for k in (-4, 3):
+        xs = bf16_bits(bf16_to_f32(x) * np.float32(2.0 ** k))
+        sk = orc.quantize_stats(xs, mode, rule)
+        f = np.array([4.0 ** k, 2.0 ** k, 2.0 ** k, 4.0 ** k, 4.0 ** k, 1.0])
+        assert np.array_equal(sk, st * f)
+    # the sign of the input does not matter; the thread split changes only rounding
+    assert np.array_equal(orc.quantize_stats(x ^ np.uint16(0x8000), mode, rule), st)
+    s8 = orc.quantize_stats(x, mode, rule, nthreads=8)
+    assert np.allclose(s8, st, rtol=n * 2.0 ** -60, atol=0)
+    assert np.array_equal(s8[:, [MAXERR, NEAR]], st[:, [MAXERR, NEAR]])
+
+
+def test_stats_poisoned_tensor_is_nan(orc):
+    x = _small("moe", (3, 24, 80)).copy()
+    x[1, 3, 7] = 0x7F80                               # +inf
+    st = orc.quantize_stats(x, "four_over_six", "mse")
+    assert np.isnan(st[1]).all() and np.isfinite(st[[0, 2]]).all()
