@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+#define NVFP4_ABI_VERSION 2
 #define NVFP4_BLOCK 16
 
 typedef enum { NVFP4_RTN6 = 0, NVFP4_FOUR_OVER_SIX = 1 } nvfp4_mode;
@@ -133,16 +133,38 @@ nvfp4_status nvfp4_fakequant_from_amax(const uint16_t* in, int64_t E, int64_t ro
                                        nvfp4_rule rule, const float* amax, uint16_t* out,
                                        float* out_alpha, hipStream_t stream);
 
+/* Columns of the per-tensor error statistics of nvfp4_quantize_diag (out_stats[E][6]). */
+enum {
+  NVFP4_STAT_SSE = 0,           /* sum of e^2 over the tensor, e = x - xhat of the chosen code */
+  NVFP4_STAT_SAE = 1,           /* sum of |e| */
+  NVFP4_STAT_MAXERR = 2,        /* max |e| (exact) */
+  NVFP4_STAT_SSE_NEAR = 3,      /* sum of e^2 over the elements with |x| > (2/3) * block max */
+  NVFP4_STAT_SSE_F32SCALE = 4,  /* sum of e^2 if each block's chosen candidate kept its
+                                   binary32 scale sigma instead of the E4M3 byte */
+  NVFP4_STAT_NEAR_COUNT = 5,    /* number of elements with |x| > (2/3) * block max (exact) */
+  NVFP4_NSTATS = 6
+};
+
 /* Diagnostics of a packed quantization (dynamic scale, E tensors): the outputs of
- * nvfp4_quantize_batched plus, per block, the block maximum it was scaled to
- * (out_qstar [E][rows][cols/16]: 4 or 6, always 6 for rtn6, 0 for a poisoned tensor) and, per
- * tensor, the number of blocks scaled to 4 (out_count4 [E], cleared by the call).  The Four
- * Over Six explainer ("Key contributions and results") expects blocks with large near-max
- * values to pick 4; this shows how often that happens on a given tensor. */
+ * nvfp4_quantize_batched plus
+ *   - per block, the block maximum it was scaled to (out_qstar [E][rows][cols/16]: 4 or 6,
+ *     always 6 for rtn6, 0 for a poisoned tensor);
+ *   - per tensor, the number of blocks scaled to 4 (out_count4 [E], cleared by the call);
+ *   - optionally (out_stats may be NULL), per tensor, the error statistics NVFP4_STAT_*
+ *     (out_stats [E][6] binary64, 8-byte aligned, cleared by the call; NaN for a poisoned
+ *     tensor).
+ * The Four Over Six explainer expects blocks with large near-max values to pick 4 ("Key
+ * contributions and results"), and reports that rounding the block scales to FP8 costs
+ * little while rounding the values between 66.6 % and 100 % of the block max drives the
+ * error ("Problem definition"): out_count4, NVFP4_STAT_SSE_NEAR and the gap between
+ * NVFP4_STAT_SSE and NVFP4_STAT_SSE_F32SCALE measure these on a given tensor.  The maximum
+ * and the count are exact; the sums are binary64 with an order that depends on the launch,
+ * within (n - 1) * 2^-53 of the exact sum relative to it (n = elements per tensor). */
 nvfp4_status nvfp4_quantize_diag(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
                                  int block, nvfp4_mode mode, nvfp4_rule rule,
                                  uint8_t* out_codes, uint8_t* out_scales, float* out_alpha,
-                                 uint8_t* out_qstar, uint32_t* out_count4, hipStream_t stream);
+                                 uint8_t* out_qstar, uint32_t* out_count4, double* out_stats,
+                                 hipStream_t stream);
 
 /* Dequantize packed NVFP4 to bf16 (for W4A16-style consumers that store 4-bit weights; the
  * Nemotron 3.5 Lightning NVFP4 news page, "two-stage QAD", quantizes the student to W4A16):

@@ -36,6 +36,9 @@ class NVFP4Error(RuntimeError):
 
 
 _lib = None
+ABI_VERSION = 2                  # NVFP4_ABI_VERSION of include/nvfp4_amax.h
+# Columns of the per-tensor statistics of quantize_diag (NVFP4_STAT_* order).
+STATS = ("sse", "sae", "maxerr", "sse_near", "sse_f32scale", "near_count")
 
 
 def lib() -> ctypes.CDLL:
@@ -48,6 +51,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.nvfp4_abi_version.restype = i32
+        if L.nvfp4_abi_version() != ABI_VERSION:
+            raise RuntimeError("libnvfp4_amax.so has ABI version %d, this binding needs %d: "
+                               "rebuild it" % (L.nvfp4_abi_version(), ABI_VERSION))
         L.nvfp4_status_str.argtypes, L.nvfp4_status_str.restype = [i32], ctypes.c_char_p
         L.nvfp4_amax.argtypes = [P, i64, i64, i64, P, P]
         L.nvfp4_quantize.argtypes = [P, i64, i64, i32, i32, i32, P, P, P, P]
@@ -57,7 +63,7 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P]
         L.nvfp4_fakequant_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
         L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i64, P, P]
-        L.nvfp4_quantize_diag.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P, P]
+        L.nvfp4_quantize_diag.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P]
         for name in ("nvfp4_quantize_diag", "nvfp4_dequantize", "nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
                      "nvfp4_fakequant_batched", "nvfp4_quantize_from_amax",
                      "nvfp4_fakequant_from_amax"):
@@ -142,19 +148,21 @@ def quantize(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=None, s
     return codes, scales, alpha
 
 
-def quantize_diag(x: torch.Tensor, mode="four_over_six", rule="mse"):
-    """Packed NVFP4 (dynamic scale) plus diagnostics -> (codes, scales, alpha, qstar, count4):
-    qstar uint8 [..., rows, cols/16] is 4 or 6 per block, count4 int32 [E] counts the blocks
-    scaled to 4."""
+def quantize_diag(x: torch.Tensor, mode="four_over_six", rule="mse", *, stats=True):
+    """Packed NVFP4 (dynamic scale) plus diagnostics ->
+    (codes, scales, alpha, qstar, count4, stats): qstar uint8 [..., rows, cols/16] is 4 or 6
+    per block, count4 int32 [E] counts the blocks scaled to 4, and stats float64 [E, 6]
+    (columns STATS; None when stats=False) holds per-tensor error statistics."""
     E, rows, cols, batched = _dims(x)
     codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, None, None, None)
     qstar = torch.empty_like(scales)
     count4 = torch.empty(E, dtype=torch.int32, device=x.device)
+    st_out = torch.empty((E, len(STATS)), dtype=torch.float64, device=x.device) if stats else None
     st = lib().nvfp4_quantize_diag(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
                                    _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(qstar),
-                                   _ptr(count4), _stream(x))
+                                   _ptr(count4), _ptr(st_out) if stats else None, _stream(x))
     _check(st, "nvfp4_quantize_diag")
-    return codes, scales, alpha, qstar, count4
+    return codes, scales, alpha, qstar, count4, st_out
 
 
 def fakequant(x: torch.Tensor, mode="four_over_six", rule="mse", *, out=None, alpha=None):

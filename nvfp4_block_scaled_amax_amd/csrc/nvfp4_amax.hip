@@ -14,6 +14,8 @@
 //                    rounding, the error reduction and the selection stay in VGPRs; codes,
 //                    scale bytes (or bf16 fake-quant values) are written with vector stores
 //   alpha_kernel     alpha[e] <- amax[e] / (6*M) once every block is done
+//   (the diagnostics variant of quantize_kernel also reduces per-tensor error statistics
+//   in binary64 and adds them with one atomic per field per workgroup)
 //
 // All floating-point steps are IEEE binary32 with round-to-nearest-even, no contraction
 // (-ffp-contract=off) and no denormal flushing; fp32 division and reciprocal are the
@@ -71,12 +73,14 @@ __device__ __forceinline__ float e2m1_value_of(uint32_t m) {
 }
 
 // ----------------------------------------------------------------------------- kernels
-__global__ void clear_kernel(uint32_t* __restrict__ acc, uint32_t* __restrict__ acc2, int64_t E) {
+__global__ void clear_kernel(uint32_t* __restrict__ acc, uint32_t* __restrict__ acc2, int64_t E,
+                             uint32_t* __restrict__ acc3, int64_t n3) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < E) {
     acc[i] = 0u;
     if (acc2) acc2[i] = 0u;
   }
+  if (acc3 && i < n3) acc3[i] = 0u;
 }
 
 // Max of two packed unsigned 16-bit lanes (v_pk_max_u16).
@@ -353,6 +357,76 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
   }
 }
 
+// ----------------------------------------------------------------------------- diagnostics
+// Per-tensor error statistics over the chosen candidate of every block (fields in the order
+// of NVFP4_STAT_*): sum e^2, sum |e|, max |e|, sum e^2 over the elements above 2/3 of their
+// block max, sum e^2 if the chosen candidate kept its binary32 block scale, and the count of
+// elements above 2/3 of their block max.  e = x - xhat is exact in binary32, so e^2 is exact
+// in binary64; the sums are binary64 (lane, then wavefront, then workgroup, then one atomic
+// per workgroup), so only their rounding depends on the order.
+struct LaneStats {
+  double sse, sae, near_sse, f32_sse;
+  float mx;
+  uint32_t near;
+};
+
+template <int SEL>
+__device__ __forceinline__ void pair_stats(uint32_t w, float xa, float xb, float d, double thr,
+                                           LaneStats& st) {
+  const f32x2 val = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);   // signed values
+  const float ea = xa - val.x * d;
+  const float eb = xb - val.y * d;
+  const double da = ea, db = eb;
+  st.sse = __builtin_fma(da, da, st.sse);
+  st.sse = __builtin_fma(db, db, st.sse);
+  st.sae = st.sae + __builtin_fabs(da);
+  st.sae = st.sae + __builtin_fabs(db);
+  st.mx = max3_abs(st.mx, ea, eb);
+  if (3.0 * (double)fabsf(xa) > thr) { st.near_sse = __builtin_fma(da, da, st.near_sse); ++st.near; }
+  if (3.0 * (double)fabsf(xb) > thr) { st.near_sse = __builtin_fma(db, db, st.near_sse); ++st.near; }
+}
+
+__device__ __forceinline__ void chosen_stats(const float (&x)[16], uint32_t w0, uint32_t w1,
+                                             float d, float bmax, LaneStats& st) {
+  const double thr = 2.0 * (double)bmax;   // 3|x| > 2 bmax, exact in binary64
+  pair_stats<0>(w0, x[0], x[1], d, thr, st);
+  pair_stats<1>(w0, x[2], x[3], d, thr, st);
+  pair_stats<2>(w0, x[4], x[5], d, thr, st);
+  pair_stats<3>(w0, x[6], x[7], d, thr, st);
+  pair_stats<0>(w1, x[8], x[9], d, thr, st);
+  pair_stats<1>(w1, x[10], x[11], d, thr, st);
+  pair_stats<2>(w1, x[12], x[13], d, thr, st);
+  pair_stats<3>(w1, x[14], x[15], d, thr, st);
+}
+
+// Sum of e^2 of one block when the candidate with target max Q (cq = RN(Q*alpha), cap its
+// largest magnitude code) keeps sigma = RN(bmax / cq) in binary32 as its block scale instead
+// of the E4M3 byte: d = RN(sigma * alpha), the rest as on the reference path.  Kept out of
+// line and rolled, re-reading the block from cache.
+__device__ __noinline__ double f32_scale_sse(const uint16_t* __restrict__ xb, float bmax,
+                                             float alpha, float cq, uint32_t cap) {
+  const float sigma = alpha == 0.0f ? 0.0f : bmax / cq;
+  const float d = sigma * alpha;
+  const float r = d == 0.0f ? 0.0f : 1.0f / d;
+  const bool r_finite = r != __builtin_inff();
+  double acc = 0.0;
+#pragma unroll 1
+  for (int i = 0; i < 16; ++i) {
+    const float x = fabsf(__uint_as_float((uint32_t)xb[i] << 16));
+    const float v = r_finite ? x * r : x / d;
+    const uint32_t m = min(e2m1_code_of(v), cap);
+    const double e = (double)(x - e2m1_value_of(m) * d);
+    acc = __builtin_fma(e, e, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
 __device__ __forceinline__ void unpack16(const uint4& p0, const uint4& p1, float (&x)[16]) {
   const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
@@ -386,7 +460,8 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     const uint4* __restrict__ in, int64_t nblk, const float* __restrict__ amax,
     uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
-    float* __restrict__ alpha_out, uint8_t* __restrict__ qstar, uint32_t* __restrict__ count4) {
+    float* __restrict__ alpha_out, uint8_t* __restrict__ qstar, uint32_t* __restrict__ count4,
+    double* __restrict__ stats) {
   __shared__ BlockTables tb;
   const int64_t t = blockIdx.y;
   const uint32_t abits = __float_as_uint(amax[t]) & 0x7FFFFFFFu;
@@ -408,6 +483,8 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   uint32_t u = blockIdx.x * kThreads + threadIdx.x;
 
   if (poison) {                                  // non-finite input or amax
+    if (DIAG && stats && blockIdx.x == 0 && threadIdx.x == 0)
+      for (int k = 0; k < NVFP4_NSTATS; ++k) stats[t * NVFP4_NSTATS + k] = __longlong_as_double(0x7FF8000000000000LL);
     for (; u < n; u += stride) {
       if (FQ) {
         const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
@@ -422,6 +499,8 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     return;
   }
   uint32_t n_four = 0;   // DIAG: blocks of this lane scaled to 4
+  LaneStats st = {0.0, 0.0, 0.0, 0.0, 0.0f, 0u};
+  const bool want_stats = DIAG && stats != nullptr;
 
   int n6, n4;
   build_tables<MODE>(tb, alpha, n6, n4);
@@ -465,6 +544,11 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
       if (DIAG) {
         qstar[base + u] = four ? 4 : 6;
         n_four += four ? 1u : 0u;
+        if (want_stats) {
+          chosen_stats(x, w0, w1, dq, bm, st);
+          st.f32_sse += f32_scale_sse(reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm,
+                                      alpha, four ? 4.0f * alpha : 6.0f * alpha, four ? 6u : 7u);
+        }
       }
     }
   }
@@ -479,6 +563,43 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
       uint32_t tot = 0;
       for (int w = 0; w < kThreads / 64; ++w) tot += wsum[w];
       if (tot) atomicAdd(count4 + t, tot);
+    }
+    if (want_stats) {
+      __shared__ double wst[kThreads / 64][5];
+      __shared__ float wmx[kThreads / 64];
+      const double v0 = wave_sum_f64(st.sse), v1 = wave_sum_f64(st.sae);
+      const double v3 = wave_sum_f64(st.near_sse), v4 = wave_sum_f64(st.f32_sse);
+      uint32_t nn = st.near;
+      float mx = st.mx;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        nn += __shfl_xor(nn, off);
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+      }
+      if ((threadIdx.x & 63) == 0) {
+        const int w = threadIdx.x >> 6;
+        wst[w][0] = v0; wst[w][1] = v1; wst[w][2] = v3; wst[w][3] = v4; wst[w][4] = (double)nn;
+        wmx[w] = mx;
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        double a[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+        float m = 0.0f;
+        for (int w = 0; w < kThreads / 64; ++w) {
+          for (int k = 0; k < 5; ++k) a[k] += wst[w][k];
+          m = fmaxf(m, wmx[w]);
+        }
+        double* o = stats + t * NVFP4_NSTATS;
+        if (a[0] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_SSE, a[0]);
+        if (a[1] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_SAE, a[1]);
+        if (a[2] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_SSE_NEAR, a[2]);
+        if (a[3] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_SSE_F32SCALE, a[3]);
+        if (a[4] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_NEAR_COUNT, a[4]);
+        // non-negative binary64 values order like their bit patterns
+        if (m != 0.0f)
+          atomicMax(reinterpret_cast<unsigned long long*>(o + NVFP4_STAT_MAXERR),
+                    (unsigned long long)__double_as_longlong((double)m));
+      }
     }
   }
 }
@@ -554,15 +675,16 @@ nvfp4_status check_common(const uint16_t* in, const Shape& s, int block, int mod
 }
 
 hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStream_t stream,
-                       uint32_t* acc2 = nullptr) {
+                       uint32_t* acc2 = nullptr, uint32_t* acc3 = nullptr, int64_t n3 = 0) {
   const int64_t chunks = s.n / 8;
   const int64_t share = std::max<int64_t>(1, kAmaxWGs / s.E);   // workgroups per tensor
   const int64_t want8 = (chunks + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
   const int64_t want1 = (chunks + kAmaxThreads - 1) / kAmaxThreads;
   const bool wide = want8 >= share;
   const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(wide ? want8 : want1, share));
-  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((s.E + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     stream, acc, acc2, s.E);
+  const int64_t nclear = std::max<int64_t>(s.E, acc3 ? n3 : 0);
+  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((nclear + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, stream, acc, acc2, s.E, acc3, n3);
   if (wide)
     hipLaunchKernelGGL(amax_kernel<8>, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
                        0, stream, reinterpret_cast<const uint4*>(in), chunks, acc);
@@ -577,7 +699,7 @@ constexpr int64_t kMaxLaunchBlocks = (INT64_C(1) << 27) - 1;   // 32-bit byte of
 template <int MODE, int RULE, bool FQ, bool DIAG>
 void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, uint8_t* codes,
                        uint8_t* scales, uint16_t* out, float* alpha_out, uint8_t* qstar,
-                       uint32_t* count4, hipStream_t stream) {
+                       uint32_t* count4, double* stats, hipStream_t stream) {
   auto launch = [&](int64_t E, int64_t nblk, int64_t first_tensor, int64_t first_block) {
     const int64_t want = (nblk + kThreads - 1) / kThreads;
     const int64_t wgs = E * nblk >= kLongLaunchBlocks ? NVFP4_BLOCK_WGS_LONG : NVFP4_BLOCK_WGS;
@@ -590,7 +712,8 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
                        scales ? scales + b0 : nullptr,
                        reinterpret_cast<uint4*>(out ? out + b0 * 16 : nullptr),
                        alpha_out ? alpha_out + first_tensor : nullptr, qstar ? qstar + b0 : nullptr,
-                       count4 ? count4 + first_tensor : nullptr);
+                       count4 ? count4 + first_tensor : nullptr,
+                       stats ? stats + first_tensor * NVFP4_NSTATS : nullptr);
   };
   if (s.nblk <= kMaxLaunchBlocks) {
     launch(s.E, s.nblk, 0, 0);
@@ -604,19 +727,19 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
 template <bool FQ, bool DIAG>
 void launch_quantize(int mode, int rule, const uint16_t* in, const Shape& s, const float* amax,
                      uint8_t* codes, uint8_t* scales, uint16_t* out, float* alpha_out,
-                     uint8_t* qstar, uint32_t* count4, hipStream_t stream) {
+                     uint8_t* qstar, uint32_t* count4, double* stats, hipStream_t stream) {
   if (mode == NVFP4_RTN6) {
     launch_quantize_t<NVFP4_RTN6, NVFP4_RULE_MSE, FQ, DIAG>(in, s, amax, codes, scales, out,
-                                                            alpha_out, qstar, count4, stream);
+                                                            alpha_out, qstar, count4, stats, stream);
   } else if (rule == NVFP4_RULE_MSE) {
     launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MSE, FQ, DIAG>(
-        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stream);
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stream);
   } else if (rule == NVFP4_RULE_MAE) {
     launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAE, FQ, DIAG>(
-        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stream);
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stream);
   } else {
     launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAXERR, FQ, DIAG>(
-        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stream);
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stream);
   }
 }
 
@@ -633,7 +756,7 @@ hipError_t launch_alpha(const uint32_t* amax_bits, float* alpha, const Shape& s,
 nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int block, int mode,
                  int rule, const float* amax_in, uint8_t* codes, uint8_t* scales, uint16_t* out,
                  float* alpha, bool fq, hipStream_t stream, uint8_t* qstar = nullptr,
-                 uint32_t* count4 = nullptr) {
+                 uint32_t* count4 = nullptr, double* stats = nullptr) {
   Shape s;
   nvfp4_status st = check_shape(E, rows, cols, &s);
   if (st != NVFP4_OK) return st;
@@ -673,12 +796,22 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
         overlap(count4, s.E * 4, codes, s.E * s.n / 2) ||
         overlap(count4, s.E * 4, scales, s.E * s.nblk) || overlap(count4, s.E * 4, alpha, s.E * 4))
       return NVFP4_ERR_ALIAS;
+    if (stats) {
+      if (!aligned(stats, 8)) return NVFP4_ERR_ALIGN;
+      const int64_t sb = s.E * NVFP4_NSTATS * 8;
+      if (overlap(stats, sb, in, in_bytes2) || overlap(stats, sb, codes, s.E * s.n / 2) ||
+          overlap(stats, sb, scales, s.E * s.nblk) || overlap(stats, sb, alpha, s.E * 4) ||
+          overlap(stats, sb, qstar, qb) || overlap(stats, sb, count4, s.E * 4))
+        return NVFP4_ERR_ALIAS;
+    }
   }
 
   (void)hipGetLastError();   // clear a stale error so the status below is this call's
   const float* amax = amax_in;
   if (!amax) {
-    if (launch_amax(in, s, reinterpret_cast<uint32_t*>(alpha), stream, count4) != hipSuccess)
+    if (launch_amax(in, s, reinterpret_cast<uint32_t*>(alpha), stream, count4,
+                    reinterpret_cast<uint32_t*>(stats), stats ? s.E * NVFP4_NSTATS * 2 : 0) !=
+        hipSuccess)
       return NVFP4_ERR_HIP;
     amax = alpha;
   }
@@ -687,13 +820,13 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
   float* alpha_in_kernel = amax == alpha ? nullptr : alpha;
   if (fq)
     launch_quantize<true, false>(mode, rule, in, s, amax, nullptr, nullptr, out, alpha_in_kernel,
-                                 nullptr, nullptr, stream);
+                                 nullptr, nullptr, nullptr, stream);
   else if (diag)
     launch_quantize<false, true>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
-                                 qstar, count4, stream);
+                                 qstar, count4, stats, stream);
   else
     launch_quantize<false, false>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
-                                  nullptr, nullptr, stream);
+                                  nullptr, nullptr, nullptr, stream);
   if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
   if (!alpha_in_kernel &&
       launch_alpha(reinterpret_cast<const uint32_t*>(amax), alpha, s, mode, stream) != hipSuccess)
@@ -790,10 +923,10 @@ NVFP4_EXPORT nvfp4_status nvfp4_quantize_diag(const uint16_t* in, int64_t E, int
                                               nvfp4_rule rule, uint8_t* out_codes,
                                               uint8_t* out_scales, float* out_alpha,
                                               uint8_t* out_qstar, uint32_t* out_count4,
-                                              hipStream_t stream) {
+                                              double* out_stats, hipStream_t stream) {
   if (!out_qstar || !out_count4) return NVFP4_ERR_NULL;
   return run(in, E, rows, cols, block, mode, rule, nullptr, out_codes, out_scales, nullptr,
-             out_alpha, false, stream, out_qstar, out_count4);
+             out_alpha, false, stream, out_qstar, out_count4, out_stats);
 }
 
 NVFP4_EXPORT nvfp4_status nvfp4_quantize_from_amax(const uint16_t* in, int64_t E, int64_t rows,

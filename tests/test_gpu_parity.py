@@ -386,11 +386,31 @@ def test_dequantize_full_size_weight(nv, orc):
 
 
 # ----------------------------------------------------------------------------- diagnostics
+MAXERR_COL, NEAR_COL = 2, 5
+
+
+def check_stats(got, ref, n, tag):
+    """Per-tensor statistics: NaN rows match, max |e| and the near-band count exactly, the
+    sums within their rounding bound.  The terms are non-negative and exact in binary64, so
+    the GPU's binary64 sums in any order are within (n-1)*2^-53 of the exact sum relative to
+    it, and the oracle's long-double sums within (n-1)*2^-64 plus one rounding to binary64."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    tol = (n - 1) * 2.0 ** -53 + (n - 1) * 2.0 ** -64 + 2.0 ** -53
+    for t in range(ref.shape[0]):
+        if np.isnan(ref[t]).any():
+            assert np.isnan(got[t]).all(), (tag, t)
+            continue
+        assert got[t, MAXERR_COL] == ref[t, MAXERR_COL], (tag, t)
+        assert got[t, NEAR_COL] == ref[t, NEAR_COL], (tag, t)
+        for k in (0, 1, 3, 4):
+            assert abs(got[t, k] - ref[t, k]) <= tol * ref[t, k], (tag, t, k, got[t, k], ref[t, k])
+
+
 @pytest.mark.parametrize("name,shape", SMALL, ids=[s[0] for s in SMALL])
 @pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
 def test_diag_choice_and_count(nv, orc, name, shape, mode, rule):
     x = W.bits(W.generate(name, shape))
-    c, s, a, q, n4 = nv.quantize_diag(to_gpu(x), mode, rule)
+    c, s, a, q, n4, st = nv.quantize_diag(to_gpu(x), mode, rule)
     torch.cuda.synchronize()
     ref = orc.quantize(x, mode, rule, want_y=False, want_qstar=True)
     assert np.array_equal(c.cpu().numpy(), ref["codes"])
@@ -401,15 +421,54 @@ def test_diag_choice_and_count(nv, orc, name, shape, mode, rule):
     assert np.array_equal(n4.cpu().numpy(), want)
     if mode == "four_over_six":
         assert want.sum() > 0
+    check_stats(st.cpu().numpy(), orc.quantize_stats(x, mode, rule, nthreads=NTHREADS),
+                x.size // E, name)
+    # without statistics the other outputs are the same
+    c2, s2, a2, q2, n42, st2 = nv.quantize_diag(to_gpu(x), mode, rule, stats=False)
+    torch.cuda.synchronize()
+    assert st2 is None and torch.equal(c2, c) and torch.equal(q2, q) and torch.equal(n42, n4)
 
 
 def test_diag_poison_and_edges(nv, orc):
     x = W.bits(W.generate("moe", (3, 16, 64))).copy()
     x[2, 3, 5] = 0x7FC0
     for name, xb in (("poison", x), ("subnormal", EDGE["subnormal"]), ("zeros", EDGE["zeros"])):
-        c, s, a, q, n4 = nv.quantize_diag(to_gpu(xb), "four_over_six", "mse")
+        c, s, a, q, n4, st = nv.quantize_diag(to_gpu(xb), "four_over_six", "mse")
         torch.cuda.synchronize()
         ref = orc.quantize(xb, "four_over_six", "mse", want_y=False, want_qstar=True)
         assert np.array_equal(q.cpu().numpy(), ref["qstar"]), name
         E = xb.shape[0] if xb.ndim == 3 else 1
         assert np.array_equal(n4.cpu().numpy(), (ref["qstar"].reshape(E, -1) == 4).sum(axis=1)), name
+        check_stats(st.cpu().numpy(), orc.quantize_stats(xb, "four_over_six", "mse"),
+                    xb.size // E, name)
+    assert np.isnan(st.cpu().numpy()).sum() == 0
+
+
+DIAG_FULL = [(w.name, mode, rule) for w in W.WORKLOADS.values()
+             for (mode, rule, _) in w.runs[:1]]
+
+
+@pytest.mark.parametrize("name,mode,rule", DIAG_FULL, ids=[c[0] for c in DIAG_FULL])
+def test_diag_stats_full_size(nv, orc, name, mode, rule):
+    """The diagnostics at full size: qstar on sampled blocks, the count of blocks scaled
+    to 4 and the error statistics of every tensor against the oracle."""
+    xt = full_input(name)
+    x = W.bits(xt)
+    E = x.shape[0] if x.ndim == 3 else 1
+    say("[diag-full] %s %s/%s" % (name, mode, rule))
+    c, s, a, q, n4, st = nv.quantize_diag(xt.cuda(), mode, rule)
+    torch.cuda.synchronize()
+    ref = orc.quantize_stats(x, mode, rule, nthreads=NTHREADS)
+    check_stats(st.cpu().numpy(), ref, x.size // E, name)
+    rng = np.random.default_rng(7)
+    ids = rng.integers(0, x.size // 16, size=4000)
+    amax = orc.amax(x, E)
+    al = np.array([orc.alpha(float(v), mode) for v in amax], np.float32)
+    rb = orc.quantize_blocks(x, al, ids, mode, rule)
+    assert np.array_equal(q.cpu().numpy().reshape(-1)[ids], rb["qstar"])
+    if mode == "four_over_six":
+        assert int(n4.sum()) > 0
+    t = st.cpu().numpy().sum(axis=0)
+    say("[diag-full] %s: near-band share of sum e^2 %.3f, scale-rounding share %.3f, "
+        "blocks scaled to 4 %.3f" % (name, t[3] / t[0], (t[0] - t[4]) / t[0],
+                                     int(n4.sum()) / (x.size // 16)))
