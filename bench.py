@@ -139,6 +139,16 @@ def main():
             nv.quantize(xs[i], args.mode, args.rule, codes=outs[i][0], scales=outs[i][1],
                         alpha=alphas[i])
 
+    ws = torch.empty(nv.FUSED_WS_WORDS * E, dtype=torch.int32, device=dev)
+
+    def fused_call(i):
+        if fq:
+            nv.fakequant_fused(xs[i], args.mode, args.rule, out=outs[i], alpha=alphas[i],
+                               workspace=ws)
+        else:
+            nv.quantize_fused(xs[i], args.mode, args.rule, codes=outs[i][0], scales=outs[i][1],
+                              alpha=alphas[i], workspace=ws)
+
     def capture(fn, count):
         """One HIP graph of `count` back-to-back calls fn(0), fn(1), ... (buffers mod R)."""
         side = torch.cuda.Stream()
@@ -192,7 +202,8 @@ def main():
                      ("rtn6_block", lambda i: block_pass(i, "rtn6", "mse")),
                      ("block_again", block_pass),          # 4/6 once more: drift check
                      ("amax", amax_pass),
-                     ("dynamic_entry_point", dynamic_call)):
+                     ("dynamic_entry_point", dynamic_call),
+                     ("fused_entry_point", fused_call)):
         g = capture(fn, B)
         legs[name] = replay_avg_us(g, B)
         del g
@@ -227,6 +238,12 @@ def main():
             "amax": {"avg_us": round(legs["amax"], 2),
                      "GBps": round(AMAX_BPE * N / (legs["amax"] * 1e-6) / 1e9, 1)},
             "dynamic_entry_point": {"avg_us": round(legs["dynamic_entry_point"], 2)},
+            "fused_entry_point": {
+                "avg_us": round(legs["fused_entry_point"], 2),
+                "blocks_per_lane": nv.fused_blocks_per_lane(wl.shape, args.mode, args.rule, fq),
+                "GBps": round(pass_bpe * N / (legs["fused_entry_point"] * 1e-6) / 1e9, 1),
+                "speedup_vs_dynamic": round(legs["dynamic_entry_point"] /
+                                            legs["fused_entry_point"], 3)},
         },
         "overhead_4over6_vs_rtn6": round(t_block / t_rtn6 - 1.0, 4),
     }

@@ -39,7 +39,8 @@
  * E = 1 for the non-batched calls.
  *
  * Ownership and ordering: every pointer is a device pointer owned by the caller.  The
- * library allocates nothing and keeps no state; calls are reentrant.  All work is
+ * library allocates nothing and keeps no state (apart from a test setting and a per-device
+ * cache of occupancy figures); calls are reentrant.  All work is
  * enqueued on `stream` (0 = the null stream) and the call returns at once; outputs are
  * defined once the stream passes the call.  During a dynamic-scale call out_alpha holds
  * the running amax, so it must not alias any other argument.  Fake-quant may run in
@@ -61,7 +62,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 2
+#define NVFP4_ABI_VERSION 3
 #define NVFP4_BLOCK 16
 
 typedef enum { NVFP4_RTN6 = 0, NVFP4_FOUR_OVER_SIX = 1 } nvfp4_mode;
@@ -165,6 +166,45 @@ nvfp4_status nvfp4_quantize_diag(const uint16_t* in, int64_t E, int64_t rows, in
                                  uint8_t* out_codes, uint8_t* out_scales, float* out_alpha,
                                  uint8_t* out_qstar, uint32_t* out_count4, double* out_stats,
                                  hipStream_t stream);
+
+/* Single-read dynamic quantization: the outputs of nvfp4_quantize_batched /
+ * nvfp4_fakequant_batched, bit for bit, reading the input from HBM once instead of twice.
+ * Because alpha depends on the whole tensor, the dynamic entry points above read every input
+ * twice (the amax pass, then the block pass).  Here each workgroup keeps its blocks on chip
+ * (VGPRs and LDS) while the tensor amax is reduced across the grid, then quantizes what it
+ * holds; the Four Over Six explainer ("Implementation details") keeps every intermediate value
+ * in registers, and this extends that across the amax dependency.
+ *   workspace  device memory of E * NVFP4_FUSED_WS_WORDS uint32 (2176 bytes per tensor,
+ *              128-byte aligned) owned by the caller; any content (the call clears it first).  Calls
+ *              that share a workspace must not overlap (calls on one stream never do).
+ * Tensors whose blocks do not fit on chip (see nvfp4_fused_single_read), and in-place
+ * fake-quant (out == in), take the two-pass path instead, with the same results; the
+ * workspace is then unused.  All workgroups of a
+ * single-read launch must be resident together; the grid is sized for that from the
+ * device's occupancy.  Their wait for each other is bounded: a workgroup that waits too long
+ * (for instance while other fused calls hold the CUs) computes the tensor amax itself from
+ * the input, so the call always completes with the same result.  Errors as above, plus
+ * NVFP4_ERR_NULL for a null workspace and NVFP4_ERR_ALIAS when it overlaps another argument. */
+#define NVFP4_FUSED_WS_WORDS 544   /* workspace words per tensor of the fused calls */
+nvfp4_status nvfp4_quantize_fused(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
+                                  int block, nvfp4_mode mode, nvfp4_rule rule,
+                                  uint8_t* out_codes, uint8_t* out_scales, float* out_alpha,
+                                  uint32_t* workspace, hipStream_t stream);
+nvfp4_status nvfp4_fakequant_fused(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
+                                   int block, nvfp4_mode mode, nvfp4_rule rule, uint16_t* out,
+                                   float* out_alpha, uint32_t* workspace, hipStream_t stream);
+
+/* For a fused call of this shape, mode, rule and output form on the current device: the
+ * number of blocks each lane holds on chip (1, 4, 12 or 28) if it reads its input once, 0 if
+ * it takes the two-pass path, or minus a status code for bad arguments.  On MI355X up to
+ * 3,670,016 blocks per tensor launch (E * rows * cols / 16; 117 MB of bf16) read once. */
+int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols, nvfp4_mode mode,
+                            nvfp4_rule rule, int fakequant);
+
+/* Test hook (process-wide, the library's only setting): how many times a workgroup of a
+ * single-read launch polls for the other workgroups (about 0.2 us each) before it computes
+ * the tensor amax itself.  0 = never wait; a negative value restores the default (2^20). */
+void nvfp4_fused_set_wait_limit(int64_t polls);
 
 /* Dequantize packed NVFP4 to bf16 (for W4A16-style consumers that store 4-bit weights; the
  * Nemotron 3.5 Lightning NVFP4 news page, "two-stage QAD", quantizes the student to W4A16):

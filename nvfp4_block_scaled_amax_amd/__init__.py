@@ -20,7 +20,8 @@ import os
 import torch
 
 __all__ = ["quantize", "fakequant", "amax", "quantize_from_amax", "fakequant_from_amax",
-           "dequantize", "quantize_diag", "lib", "NVFP4Error", "MODES", "RULES", "LIB_PATH"]
+           "dequantize", "quantize_diag", "quantize_fused", "fakequant_fused",
+           "fused_blocks_per_lane", "set_fused_wait_limit", "lib", "NVFP4Error", "MODES", "RULES", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_amax.so")
 MODES = {"rtn6": 0, "four_over_six": 1}
@@ -36,7 +37,8 @@ class NVFP4Error(RuntimeError):
 
 
 _lib = None
-ABI_VERSION = 2                  # NVFP4_ABI_VERSION of include/nvfp4_amax.h
+ABI_VERSION = 3                  # NVFP4_ABI_VERSION of include/nvfp4_amax.h
+FUSED_WS_WORDS = 544             # NVFP4_FUSED_WS_WORDS: workspace int32 words per tensor
 # Columns of the per-tensor statistics of quantize_diag (NVFP4_STAT_* order).
 STATS = ("sse", "sae", "maxerr", "sse_near", "sse_f32scale", "near_count")
 
@@ -64,7 +66,13 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_fakequant_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
         L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i64, P, P]
         L.nvfp4_quantize_diag.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P]
-        for name in ("nvfp4_quantize_diag", "nvfp4_dequantize", "nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
+        L.nvfp4_quantize_fused.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P]
+        L.nvfp4_fakequant_fused.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
+        L.nvfp4_fused_single_read.argtypes = [i64, i64, i64, i32, i32, i32]
+        L.nvfp4_fused_single_read.restype = i32
+        L.nvfp4_fused_set_wait_limit.argtypes = [i64]
+        L.nvfp4_fused_set_wait_limit.restype = None
+        for name in ("nvfp4_quantize_fused", "nvfp4_fakequant_fused", "nvfp4_quantize_diag", "nvfp4_dequantize", "nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
                      "nvfp4_fakequant_batched", "nvfp4_quantize_from_amax",
                      "nvfp4_fakequant_from_amax"):
             getattr(L, name).restype = i32
@@ -226,3 +234,62 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, *
     _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(alpha), E, rows, cols,
                                   _ptr(out), _stream(codes)), "nvfp4_dequantize")
     return out
+
+
+# ----------------------------------------------------------------------------- single read
+def _workspace(workspace, E, x):
+    if workspace is None:
+        return torch.empty(FUSED_WS_WORDS * E, dtype=torch.int32, device=x.device)
+    if (workspace.device != x.device or workspace.dtype not in (torch.int32, torch.uint32)
+            or workspace.numel() < FUSED_WS_WORDS * E or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous int32 tensor of %d*E elements on x's "
+                         "device" % FUSED_WS_WORDS)
+    return workspace
+
+
+def quantize_fused(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=None,
+                   scales=None, alpha=None, workspace=None):
+    """Packed NVFP4 with a dynamic scale, reading x once when it fits on chip -> (codes,
+    scales, alpha), identical to quantize().  workspace: int32 [FUSED_WS_WORDS * E], 128-byte
+    aligned (allocated here if None)."""
+    E, rows, cols, batched = _dims(x)
+    codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha)
+    ws = _workspace(workspace, E, x)
+    st = lib().nvfp4_quantize_fused(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                    _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(ws), _stream(x))
+    _check(st, "nvfp4_quantize_fused")
+    return codes, scales, alpha
+
+
+def fakequant_fused(x: torch.Tensor, mode="four_over_six", rule="mse", *, out=None, alpha=None,
+                    workspace=None):
+    """bf16 quantize-dequantize with a dynamic scale, reading x once when it fits on chip ->
+    (y, alpha), identical to fakequant()."""
+    E, rows, cols, batched = _dims(x)
+    out = _out(out, x.shape, torch.bfloat16, x)
+    alpha = _out(alpha, (E,), torch.float32, x)
+    ws = _workspace(workspace, E, x)
+    st = lib().nvfp4_fakequant_fused(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                     _ptr(out), _ptr(alpha), _ptr(ws), _stream(x))
+    _check(st, "nvfp4_fakequant_fused")
+    return out, alpha
+
+
+def fused_blocks_per_lane(shape, mode="four_over_six", rule="mse", fakequant=False) -> int:
+    """Blocks each lane holds on chip in a fused call of this shape (1, 4, 12 or 28), or 0 when
+    the call takes the two-pass path (on the current device)."""
+    shape = tuple(shape)
+    if len(shape) not in (2, 3):
+        raise ValueError("shape must be (rows, cols) or (E, rows, cols)")
+    E = shape[0] if len(shape) == 3 else 1
+    r = lib().nvfp4_fused_single_read(E, shape[-2], shape[-1], _mode(mode), _rule(rule),
+                                      int(bool(fakequant)))
+    if r < 0:
+        raise ValueError("nvfp4_fused_single_read: %s" % lib().nvfp4_status_str(-r).decode())
+    return int(r)
+
+
+def set_fused_wait_limit(polls: int) -> None:
+    """Test hook: polls before a fused workgroup stops waiting for the others and computes the
+    tensor amax itself (0 = never wait, negative = the default)."""
+    lib().nvfp4_fused_set_wait_limit(int(polls))

@@ -16,6 +16,10 @@
 //   alpha_kernel     alpha[e] <- amax[e] / (6*M) once every block is done
 //   (the diagnostics variant of quantize_kernel also reduces per-tensor error statistics
 //   in binary64 and adds them with one atomic per field per workgroup)
+//   fused_kernel     single-read dynamic quantization for tensors that fit on chip: loads
+//                    and keeps each lane's blocks (VGPRs + LDS), reduces amax, waits for
+//                    every workgroup of the tensor at a grid-wide counter, then runs the
+//                    block pass on the blocks it holds
 //
 // All floating-point steps are IEEE binary32 with round-to-nearest-even, no contraction
 // (-ffp-contract=off) and no denormal flushing; fp32 division and reciprocal are the
@@ -24,6 +28,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "nvfp4_amax.h"
 
@@ -604,6 +609,232 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------- fused path
+// Single-read dynamic quantization.  alpha depends on the whole tensor, so the two-pass path
+// reads the input twice (amax pass, block pass).  Here each lane keeps its blocks on chip
+// between the two phases: KR blocks in VGPRs and KL in LDS, blocks (k*G + g)*256 + lane for
+// k < KR + KL (coalesced per k).  Phase 1 loads them and reduces the magnitude max.  The
+// workgroups of a tensor then meet at a two-level counter in the caller's workspace; the last
+// to arrive publishes amax, and each workgroup runs the block pass on the blocks it holds.
+// The host sizes the grid so that every workgroup can be resident at once.  The wait is
+// bounded: after `wait_limit` polls a workgroup computes the tensor amax itself from the input
+// (the same exact value), so every wave exits whatever the scheduling.
+//
+// Workspace of one tensor (kFusedWsWords words, zeroed before the launch), one 128-byte line
+// per group so that arrivals and polls spread over many lines: workgroup g belongs to group
+// g % S (S = min(16, G)); line i holds the group's max (atomicMax), arrival count and ready
+// flag; the top line holds the max and count over the groups.  The workgroup that completes a
+// group forwards the group max to the top line; the one that completes the top line writes
+// (amax | 1) into every group's flag (amax bits have 16 zero low bits), so a poller needs
+// nothing else from memory.  All of it is relaxed device-scope atomics: an acquire or release
+// at device scope writes back and invalidates the L2 of the XCD, which at a thousand
+// workgroups cost more than 100 us.  With at least 8 workgroups per group and at most 16
+// groups, a launch of fewer than 16 workgroups uses one group and no top level.  The one
+// ordering needed -- a workgroup's max is performed
+// before its count -- comes from issuing the count only after the returning atomicMax is back
+// (a register dependency on its result); a group's completer reads the group max only after
+// its own count returned, so every member's max is in.
+constexpr uint32_t kFusedDefaultWaitLimit = 1u << 20;   // polls of ~1 us (a device-scope load
+                                                         // and a short sleep): about 1 s
+constexpr int kFusedGroups = 16;
+constexpr int kLineWords = 32;                           // 128 bytes
+constexpr int64_t kFusedWsWords = (kFusedGroups + 1) * kLineWords;
+static_assert(kFusedWsWords == NVFP4_FUSED_WS_WORDS, "workspace size of the fused calls");
+
+// Magnitude max of tensor t computed by one workgroup alone (the fallback of the wait).
+__device__ __noinline__ uint32_t wg_tensor_amax(const uint4* __restrict__ p, int64_t chunks,
+                                                uint32_t* part) {
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < chunks; i += kThreads) m = mag_max8(m, p[i]);
+  m = max(m & 0xFFFFu, m >> 16) << 16;
+  m = wave_max_u32(m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = part[0];
+  for (int w = 1; w < kThreads / 64; ++w) r = max(r, part[w]);
+  return r;
+}
+
+// Block pass of one block held on chip: the same steps and stores as quantize_kernel.
+template <int MODE, int RULE, bool FQ>
+__device__ __forceinline__ void fused_emit(const uint4& c0, const uint4& c1, uint32_t u,
+                                           const char* inT, char* codesT, uint8_t* scalesT,
+                                           char* outT, const BlockTables& tb, int n6, int n4,
+                                           float alpha, bool tiny_alpha) {
+  float x[16];
+  unpack16(c0, c1, x);
+  uint32_t sc, w0, w1;
+  float dq, bm;
+  bool slow, four;
+  fast_block<MODE, RULE>(x, tb, n6, n4, slow, sc, dq, w0, w1, bm, four);
+  if (slow || tiny_alpha) {
+    const RefOut o =
+        ref_block<MODE, RULE>(reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm, alpha);
+    sc = o.s;
+    dq = o.d;
+    w0 = o.w0;
+    w1 = o.w1;
+  }
+  if (FQ) {
+    uint32_t y[8];
+    dequant_bf16(w0, w1, dq, y);
+    *reinterpret_cast<uint4*>(outT + (u << 5)) = make_uint4(y[0], y[1], y[2], y[3]);
+    *reinterpret_cast<uint4*>(outT + (u << 5) + 16) = make_uint4(y[4], y[5], y[6], y[7]);
+  } else {
+    *reinterpret_cast<uint2*>(codesT + (u << 3)) = make_uint2(w0, w1);
+    scalesT[u] = (uint8_t)sc;
+  }
+}
+
+template <bool FQ>
+__device__ __forceinline__ void fused_poison(uint32_t u, char* codesT, uint8_t* scalesT,
+                                             char* outT) {
+  if (FQ) {
+    const uint4 nan4 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    *reinterpret_cast<uint4*>(outT + (u << 5)) = nan4;
+    *reinterpret_cast<uint4*>(outT + (u << 5) + 16) = nan4;
+  } else {
+    *reinterpret_cast<uint2*>(codesT + (u << 3)) = make_uint2(0u, 0u);
+    scalesT[u] = 0x7F;
+  }
+}
+
+// Grid: x = G workgroups per tensor, y = tensor.  nblk <= (KR + KL) * G * 256 per tensor and
+// nblk < 2^27 (the host checks both).
+template <int MODE, int RULE, bool FQ, int KR, int KL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fused_kernel(
+    const uint4* __restrict__ in, int64_t nblk, uint32_t* __restrict__ ws,
+    uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
+    float* __restrict__ alpha_out, uint32_t wait_limit) {
+  __shared__ BlockTables tb;
+  __shared__ uint4 held[KL > 0 ? KL : 1][2][kThreads];
+  __shared__ uint32_t part[kThreads / 64];
+  __shared__ uint32_t amax_sh;
+  const int64_t t = blockIdx.y;
+  const uint32_t G = gridDim.x, g = blockIdx.x, tid = threadIdx.x;
+  const int64_t base = t * nblk;
+  const char* inT = reinterpret_cast<const char*>(in + 2 * base);
+  char* codesT = reinterpret_cast<char*>(codes + base);
+  uint8_t* scalesT = scales + base;
+  char* outT = reinterpret_cast<char*>(out + 2 * base);
+  const uint32_t n = (uint32_t)nblk;
+
+  // phase 1: load every held block (all loads in flight together), magnitude max
+  uint4 r0[KR], r1[KR], l0[KL > 0 ? KL : 1], l1[KL > 0 ? KL : 1];
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const uint32_t u = ((uint32_t)k * G + g) * kThreads + tid;
+    r0[k] = r1[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (u < n) {
+      r0[k] = *reinterpret_cast<const uint4*>(inT + (u << 5));
+      r1[k] = *reinterpret_cast<const uint4*>(inT + (u << 5) + 16);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KL; ++k) {
+    const uint32_t u = ((uint32_t)(KR + k) * G + g) * kThreads + tid;
+    l0[k] = l1[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (u < n) {
+      l0[k] = *reinterpret_cast<const uint4*>(inT + (u << 5));
+      l1[k] = *reinterpret_cast<const uint4*>(inT + (u << 5) + 16);
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < KR; ++k) m = mag_max8(mag_max8(m, r0[k]), r1[k]);
+#pragma unroll
+  for (int k = 0; k < KL; ++k) {
+    m = mag_max8(mag_max8(m, l0[k]), l1[k]);
+    held[k][0][tid] = l0[k];
+    held[k][1][tid] = l1[k];
+  }
+  m = max(m & 0xFFFFu, m >> 16) << 16;
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0) part[tid >> 6] = m;
+  __syncthreads();
+
+  // arrival and the grid-wide wait (one lane), bounded
+  if (tid == 0) {
+    uint32_t wgm = part[0];
+    for (int w = 1; w < kThreads / 64; ++w) wgm = max(wgm, part[w]);
+    // groups of at least 8 workgroups, at most 16 groups; one group needs no top level
+    const uint32_t S = min((uint32_t)kFusedGroups, max(1u, G / 8u));
+    const uint32_t grp = g % S;
+    uint32_t* wt = ws + t * kFusedWsWords;
+    uint32_t* line = wt + grp * kLineWords;                // [0] max, [1] count, [2] flag
+    uint32_t* top = wt + kFusedGroups * kLineWords;        // [0] max, [1] count
+    const uint32_t members = (G - grp + S - 1) / S;
+    const uint32_t prev =
+        __hip_atomic_fetch_max(line, wgm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t one;
+    asm volatile("v_mov_b32 %0, 1" : "=v"(one) : "v"(prev));   // waits for the max to return
+    if (__hip_atomic_fetch_add(line + 1, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        members - 1) {                                          // this group is complete
+      const uint32_t gm = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (S == 1) {                                             // the only group: publish
+        __hip_atomic_store(line + 2, gm | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        const uint32_t prev2 =
+            __hip_atomic_fetch_max(top, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t one2;
+        asm volatile("v_mov_b32 %0, 1" : "=v"(one2) : "v"(prev2));
+        if (__hip_atomic_fetch_add(top + 1, one2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            S - 1) {                                            // every group is complete
+          const uint32_t ready =
+              __hip_atomic_load(top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) | 1u;
+          for (uint32_t i = 0; i < S; ++i)
+            __hip_atomic_store(wt + i * kLineWords + 2, ready, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    uint32_t polls = 0, flag;
+    while (!((flag = __hip_atomic_load(line + 2, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)) & 1u)) {
+      if (polls++ >= wait_limit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    amax_sh = (flag & 1u) ? (flag & ~1u) : 0xFFFFFFFFu;   // 0xFFFFFFFF: "compute it here"
+  }
+  __syncthreads();
+  uint32_t abits = amax_sh;
+  if (abits == 0xFFFFFFFFu)
+    abits = wg_tensor_amax(reinterpret_cast<const uint4*>(inT), nblk * 2, part);
+
+  // phase 2: the block pass on the held blocks
+  const bool poison = abits >= 0x7F800000u;
+  const float alpha =
+      poison ? 0.0f : __uint_as_float(abits) / (MODE == NVFP4_FOUR_OVER_SIX ? kC6x256 : kC6x448);
+  if (g == 0 && tid == 0) alpha_out[t] = poison ? __uint_as_float(0x7FC00000u) : alpha;
+  if (poison) {
+#pragma unroll
+    for (int k = 0; k < KR + KL; ++k) {
+      const uint32_t u = ((uint32_t)k * G + g) * kThreads + tid;
+      if (u < n) fused_poison<FQ>(u, codesT, scalesT, outT);
+    }
+    return;
+  }
+  int n6, n4;
+  build_tables<MODE>(tb, alpha, n6, n4);
+  __syncthreads();
+  const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const uint32_t u = ((uint32_t)k * G + g) * kThreads + tid;
+    if (u < n)
+      fused_emit<MODE, RULE, FQ>(r0[k], r1[k], u, inT, codesT, scalesT, outT, tb, n6, n4,
+                                 alpha, tiny_alpha);
+  }
+#pragma unroll
+  for (int k = 0; k < KL; ++k) {
+    const uint32_t u = ((uint32_t)(KR + k) * G + g) * kThreads + tid;
+    if (u < n)
+      fused_emit<MODE, RULE, FQ>(held[k][0][tid], held[k][1][tid], u, inT, codesT, scalesT,
+                                 outT, tb, n6, n4, alpha, tiny_alpha);
+  }
+}
+
 // Dequantize: packed codes + scale bytes + alpha -> bf16, one block per lane per step.
 // d = RN(dec(s) * alpha) and y = bf16(RN(val(code) * d)): the values the fake-quant output
 // holds for the tensor that was quantized.  A NaN alpha or scale byte gives NaN (0x7FC0).
@@ -753,11 +984,13 @@ hipError_t launch_alpha(const uint32_t* amax_bits, float* alpha, const Shape& s,
 
 // Shared body of every packed / fake-quant entry point.  amax_in == nullptr: dynamic scale
 // (out_alpha is the amax accumulator); otherwise the caller's amax.
-nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int block, int mode,
-                 int rule, const float* amax_in, uint8_t* codes, uint8_t* scales, uint16_t* out,
-                 float* alpha, bool fq, hipStream_t stream, uint8_t* qstar = nullptr,
-                 uint32_t* count4 = nullptr, double* stats = nullptr) {
-  Shape s;
+// Arguments shared by every packed / fake-quant entry point: shape, enums, the outputs of the
+// chosen form (packed or fake-quant), alignment and overlaps.
+nvfp4_status validate_main(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int block,
+                           int mode, int rule, const float* amax_in, const uint8_t* codes,
+                           const uint8_t* scales, const uint16_t* out, const float* alpha, bool fq,
+                           Shape* sp) {
+  Shape& s = *sp;
   nvfp4_status st = check_shape(E, rows, cols, &s);
   if (st != NVFP4_OK) return st;
   st = check_common(in, s, block, mode, rule);
@@ -784,6 +1017,17 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
                     overlap(scales, sb, amax_in, alpha_bytes)))
       return NVFP4_ERR_ALIAS;
   }
+  return NVFP4_OK;
+}
+
+nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int block, int mode,
+                 int rule, const float* amax_in, uint8_t* codes, uint8_t* scales, uint16_t* out,
+                 float* alpha, bool fq, hipStream_t stream, uint8_t* qstar = nullptr,
+                 uint32_t* count4 = nullptr, double* stats = nullptr) {
+  Shape s;
+  nvfp4_status st = validate_main(in, E, rows, cols, block, mode, rule, amax_in, codes, scales,
+                                  out, alpha, fq, &s);
+  if (st != NVFP4_OK) return st;
 
   const bool diag = qstar != nullptr;
   if (diag) {
@@ -832,6 +1076,121 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
       launch_alpha(reinterpret_cast<const uint32_t*>(amax), alpha, s, mode, stream) != hipSuccess)
     return NVFP4_ERR_HIP;
   return NVFP4_OK;
+}
+
+// ----------------------------------------------------------------------------- fused (host)
+std::atomic<uint32_t> g_wait_limit{kFusedDefaultWaitLimit};
+
+// Workgroups of one fused_kernel instance that fit on the current device at once (occupancy
+// per CU times the CU count), cached per device; 0 if unknown.
+template <int MODE, int RULE, bool FQ, int KR, int KL>
+int64_t fused_resident_wgs() {
+  static std::atomic<int64_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v != 0) return v > 0 ? v : 0;
+  int per_cu = 0, cus = 0;
+  const bool ok =
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&fused_kernel<MODE, RULE, FQ, KR, KL>), kThreads,
+          0) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+  v = ok ? (int64_t)per_cu * cus : 0;
+  cache[dev].store(v > 0 ? v : -1, std::memory_order_relaxed);
+  return v > 0 ? v : 0;
+}
+
+// Workgroups per tensor for one tier, or 0 when the tensors do not fit on chip with it.
+template <int MODE, int RULE, bool FQ, int KR, int KL>
+int64_t fused_tier_wgs(const Shape& s) {
+  constexpr int64_t per_wg = (int64_t)(KR + KL) * kThreads;
+  const int64_t G = (s.nblk + per_wg - 1) / per_wg;
+  return G * s.E <= fused_resident_wgs<MODE, RULE, FQ, KR, KL>() ? G : 0;
+}
+
+template <int MODE, int RULE, bool FQ, int KR, int KL>
+void fused_launch(int64_t G, const uint16_t* in, const Shape& s, uint32_t* ws, uint8_t* codes,
+                  uint8_t* scales, uint16_t* out, float* alpha, hipStream_t stream) {
+  const int64_t words = s.E * kFusedWsWords;
+  hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((words + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, ws, nullptr, words, nullptr, (int64_t)0);
+  hipLaunchKernelGGL((fused_kernel<MODE, RULE, FQ, KR, KL>), dim3((unsigned)G, (unsigned)s.E),
+                     dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(in), s.nblk, ws,
+                     reinterpret_cast<uint2*>(codes), scales, reinterpret_cast<uint4*>(out), alpha,
+                     g_wait_limit.load(std::memory_order_relaxed));
+}
+
+// Tiers of blocks held per lane: (KR in VGPRs, KL in LDS) = (1,0), (4,0), (12,0), (20,8).  The
+// first that fits runs (more workgroups for smaller tensors).  Returns the blocks held per lane,
+// or 0 when no tier fits.
+template <int MODE, int RULE, bool FQ>
+int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uint8_t* codes,
+               uint8_t* scales, uint16_t* out, float* alpha, hipStream_t stream) {
+  if (s.nblk > kMaxLaunchBlocks) return 0;
+  int64_t G;
+  if ((G = fused_tier_wgs<MODE, RULE, FQ, 1, 0>(s)) > 0) {
+    if (launch) fused_launch<MODE, RULE, FQ, 1, 0>(G, in, s, ws, codes, scales, out, alpha, stream);
+    return 1;
+  }
+  if ((G = fused_tier_wgs<MODE, RULE, FQ, 4, 0>(s)) > 0) {
+    if (launch) fused_launch<MODE, RULE, FQ, 4, 0>(G, in, s, ws, codes, scales, out, alpha, stream);
+    return 4;
+  }
+  if ((G = fused_tier_wgs<MODE, RULE, FQ, 12, 0>(s)) > 0) {
+    if (launch) fused_launch<MODE, RULE, FQ, 12, 0>(G, in, s, ws, codes, scales, out, alpha, stream);
+    return 12;
+  }
+  if ((G = fused_tier_wgs<MODE, RULE, FQ, 20, 8>(s)) > 0) {
+    if (launch) fused_launch<MODE, RULE, FQ, 20, 8>(G, in, s, ws, codes, scales, out, alpha, stream);
+    return 28;
+  }
+  return 0;
+}
+
+template <bool FQ>
+int fused_dispatch(bool launch, int mode, int rule, const uint16_t* in, const Shape& s,
+                    uint32_t* ws, uint8_t* codes, uint8_t* scales, uint16_t* out, float* alpha,
+                    hipStream_t stream) {
+  if (mode == NVFP4_RTN6)
+    return fused_try<NVFP4_RTN6, NVFP4_RULE_MSE, FQ>(launch, in, s, ws, codes, scales, out, alpha,
+                                                     stream);
+  if (rule == NVFP4_RULE_MSE)
+    return fused_try<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MSE, FQ>(launch, in, s, ws, codes, scales,
+                                                              out, alpha, stream);
+  if (rule == NVFP4_RULE_MAE)
+    return fused_try<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAE, FQ>(launch, in, s, ws, codes, scales,
+                                                              out, alpha, stream);
+  return fused_try<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAXERR, FQ>(launch, in, s, ws, codes, scales,
+                                                               out, alpha, stream);
+}
+
+nvfp4_status run_fused(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int block,
+                       int mode, int rule, uint8_t* codes, uint8_t* scales, uint16_t* out,
+                       float* alpha, uint32_t* ws, bool fq, hipStream_t stream) {
+  Shape s;
+  nvfp4_status st = validate_main(in, E, rows, cols, block, mode, rule, nullptr, codes, scales,
+                                  out, alpha, fq, &s);
+  if (st != NVFP4_OK) return st;
+  if (!ws) return NVFP4_ERR_NULL;
+  if (!aligned(ws, 128)) return NVFP4_ERR_ALIGN;
+  const int64_t wb = s.E * kFusedWsWords * 4, in_bytes = s.E * s.n * 2;
+  if (overlap(ws, wb, in, in_bytes) || overlap(ws, wb, alpha, s.E * 4) ||
+      (fq ? overlap(ws, wb, out, in_bytes)
+          : (overlap(ws, wb, codes, s.E * s.n / 2) || overlap(ws, wb, scales, s.E * s.nblk))))
+    return NVFP4_ERR_ALIAS;
+  (void)hipGetLastError();
+  // In-place fake-quant takes the two-pass path: a workgroup that stops waiting re-reads the
+  // whole input, which other workgroups may already be overwriting.
+  const int fused = fq && out == in ? 0
+                  : fq ? fused_dispatch<true>(true, mode, rule, in, s, ws, nullptr, nullptr,
+                                               out, alpha, stream)
+                        : fused_dispatch<false>(true, mode, rule, in, s, ws, codes, scales,
+                                                nullptr, alpha, stream);
+  if (!fused)   // too large to hold on chip: the two-pass path (the workspace is not used)
+    return run(in, E, rows, cols, block, mode, rule, nullptr, codes, scales, out, alpha, fq,
+               stream);
+  return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
 }  // namespace
@@ -947,4 +1306,41 @@ NVFP4_EXPORT nvfp4_status nvfp4_fakequant_from_amax(const uint16_t* in, int64_t 
   if (!amax) return NVFP4_ERR_NULL;
   return run(in, E, rows, cols, block, mode, rule, amax, nullptr, nullptr, out, out_alpha, true,
              stream);
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_quantize_fused(const uint16_t* in, int64_t E, int64_t rows,
+                                               int64_t cols, int block, nvfp4_mode mode,
+                                               nvfp4_rule rule, uint8_t* out_codes,
+                                               uint8_t* out_scales, float* out_alpha,
+                                               uint32_t* workspace, hipStream_t stream) {
+  return run_fused(in, E, rows, cols, block, mode, rule, out_codes, out_scales, nullptr,
+                   out_alpha, workspace, false, stream);
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_fakequant_fused(const uint16_t* in, int64_t E, int64_t rows,
+                                                int64_t cols, int block, nvfp4_mode mode,
+                                                nvfp4_rule rule, uint16_t* out, float* out_alpha,
+                                                uint32_t* workspace, hipStream_t stream) {
+  return run_fused(in, E, rows, cols, block, mode, rule, nullptr, nullptr, out, out_alpha,
+                   workspace, true, stream);
+}
+
+NVFP4_EXPORT int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols,
+                                         nvfp4_mode mode, nvfp4_rule rule, int fakequant) {
+  Shape s;
+  nvfp4_status st = check_shape(E, rows, cols, &s);
+  if (st != NVFP4_OK) return -(int)st;
+  if ((mode != NVFP4_RTN6 && mode != NVFP4_FOUR_OVER_SIX) ||
+      (rule != NVFP4_RULE_MSE && rule != NVFP4_RULE_MAE && rule != NVFP4_RULE_MAXERR))
+    return -(int)NVFP4_ERR_ENUM;
+  return fakequant ? fused_dispatch<true>(false, mode, rule, nullptr, s, nullptr, nullptr, nullptr,
+                                          nullptr, nullptr, nullptr)
+                   : fused_dispatch<false>(false, mode, rule, nullptr, s, nullptr, nullptr,
+                                           nullptr, nullptr, nullptr, nullptr);
+}
+
+NVFP4_EXPORT void nvfp4_fused_set_wait_limit(int64_t polls) {
+  g_wait_limit.store(polls < 0 ? kFusedDefaultWaitLimit
+                               : (uint32_t)std::min<int64_t>(polls, 0xFFFFFFFFll),
+                     std::memory_order_relaxed);
 }

@@ -32,7 +32,7 @@ def L():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|int|const char\*)\s+(nvfp4_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:nvfp4_status|int|void|const char\*)\s+(nvfp4_\w+)\s*\(",
                                  text, re.M)))
 
 
@@ -42,13 +42,15 @@ def test_header_declares_the_entry_points():
                             "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
                             "nvfp4_fakequant_batched", "nvfp4_quantize_from_amax",
                             "nvfp4_fakequant_from_amax", "nvfp4_dequantize",
-                            "nvfp4_quantize_diag"])
+                            "nvfp4_quantize_diag", "nvfp4_quantize_fused",
+                            "nvfp4_fakequant_fused", "nvfp4_fused_single_read",
+                            "nvfp4_fused_set_wait_limit"])
 
 
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.nvfp4_abi_version() == 2
+    assert L.nvfp4_abi_version() == 3
     for st in range(8):
         assert L.nvfp4_status_str(st)
     assert L.nvfp4_status_str(99) == b"unknown status"
@@ -133,6 +135,25 @@ def test_diag_validation(L):
     assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 132, None) == EALIGN   # stats
     assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 64, None) == EALIAS    # over count4
     assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, A + 64, None) == EALIAS    # in input
+
+
+def test_fused_validation(L):
+    fq = L.nvfp4_quantize_fused
+    ff = L.nvfp4_fakequant_fused
+    W = 0x2100000
+    assert fq(A, 1, 4, 32, 16, 1, 0, B, C, D, None, None) == ENULL          # no workspace
+    assert fq(A, 1, 4, 32, 16, 1, 0, B, C, D, W + 64, None) == EALIGN       # 128-byte lines
+    assert fq(A, 1, 4, 32, 16, 1, 0, B, C, D, A + 128, None) == EALIAS      # in the input
+    assert fq(A, 1, 4, 32, 16, 1, 0, B, C, D, D, None) == EALIAS            # over alpha
+    assert fq(A, 1, 4, 32, 16, 1, 0, B, C, D, C - 128, None) == EALIAS      # over the scales
+    assert fq(A, 1, 4, 30, 16, 1, 0, B, C, D, W, None) == ESHAPE
+    assert fq(A, 1, 4, 32, 16, 2, 0, B, C, D, W, None) == EENUM
+    assert ff(A, 1, 4, 32, 16, 1, 0, B, D, None, None) == ENULL
+    assert ff(A, 1, 4, 32, 16, 1, 0, B, D, B, None) == EALIAS              # over the output
+    # the shape query needs no GPU for argument errors
+    assert L.nvfp4_fused_single_read(1, 4, 30, 1, 0, 0) == -ESHAPE
+    assert L.nvfp4_fused_single_read(1, 4, 32, 3, 0, 0) == -EENUM
+    assert L.nvfp4_fused_single_read(0, 4, 32, 1, 0, 0) == -ESHAPE
 
 
 def test_python_binding_checks_inputs():

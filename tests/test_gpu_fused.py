@@ -1,0 +1,161 @@
+"""Single-read (fused) dynamic quantization on the GPU, through the C ABI, against the oracle.
+
+The fused entry points must give the dynamic entry points' results bit for bit: codes, scale
+bytes, alpha bits and fake-quant bf16 bits equal to the oracle's.  Covered here: every tier of
+blocks held per lane (1, 4, 12 and 28, confirmed through the shape query), the batched form,
+the edge tensors, poisoning, the bounded grid-wide wait forced from the host (every workgroup
+or some of them computing the tensor amax alone), the two-pass route for tensors that do not
+fit on chip and for in-place fake-quant, and a workspace that starts with arbitrary content."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_amax_amd import workloads as W
+from test_gpu_parity import EDGE, RUNS, SMALL, to_gpu, u16
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def nv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import nvfp4_block_scaled_amax_amd as m
+    m.lib()
+    yield m
+    m.set_fused_wait_limit(-1)
+
+
+def run_fused(nv, x_bits, mode, rule, fq, workspace=None):
+    xg = to_gpu(x_bits)
+    if fq:
+        y, al = nv.fakequant_fused(xg, mode, rule, workspace=workspace)
+        torch.cuda.synchronize()
+        return dict(y=u16(y), alpha=al.cpu().numpy())
+    c, s, al = nv.quantize_fused(xg, mode, rule, workspace=workspace)
+    torch.cuda.synchronize()
+    return dict(codes=c.cpu().numpy(), scales=s.cpu().numpy(), alpha=al.cpu().numpy())
+
+
+def assert_matches_oracle(orc, x_bits, got, mode, rule, fq, tag):
+    ref = orc.quantize(x_bits, mode, rule, nthreads=NTHREADS, want_y=fq)
+    E = x_bits.shape[0] if x_bits.ndim == 3 else 1
+    assert np.array_equal(got["alpha"].view(np.uint32), ref["alpha"][:E].view(np.uint32)), tag
+    if fq:
+        assert np.array_equal(got["y"], ref["y"]), tag
+    else:
+        assert np.array_equal(got["codes"], ref["codes"]), tag
+        assert np.array_equal(got["scales"], ref["scales"]), tag
+
+
+@pytest.mark.parametrize("name,shape", SMALL, ids=[s[0] for s in SMALL])
+@pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
+@pytest.mark.parametrize("fq", [False, True], ids=["packed", "fakequant"])
+def test_fused_small_whole(nv, orc, name, shape, mode, rule, fq):
+    x = W.bits(W.generate(name, shape))
+    assert nv.fused_blocks_per_lane(shape, mode, rule, fq) >= 1
+    assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq, name)
+
+
+# Shapes that select each tier on a 256-CU MI355X (the test checks the tier it gets).
+TIERS = [(1, (256, 256)), (4, (1024, 8208)), (12, (4096, 8448)), (28, (4096, 14336))]
+
+
+@pytest.mark.parametrize("tier,shape", TIERS, ids=["tier%d" % t for t, _ in TIERS])
+@pytest.mark.parametrize("mode,rule,fq", [("four_over_six", "mse", False),
+                                          ("rtn6", "mse", True),
+                                          ("four_over_six", "mae", True)],
+                         ids=["46mse-packed", "rtn6-fq", "46mae-fq"])
+def test_fused_tiers_whole_tensor(nv, orc, tier, shape, mode, rule, fq):
+    got_tier = nv.fused_blocks_per_lane(shape, mode, rule, fq)
+    say("[fused] %s %s/%s fq=%s: %d blocks per lane" % (shape, mode, rule, fq, got_tier))
+    if tier == 28 and got_tier == 0:
+        pytest.fail("the weight-sized tensor does not fit on chip on this device")
+    assert got_tier >= 1
+    if tier in (1, 28):
+        assert got_tier == tier, got_tier
+    x = W.bits(W.weight(shape, seed=300 + tier))
+    assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq,
+                          "tier%d" % tier)
+
+
+def test_fused_tiers_are_all_exercised(nv):
+    seen = {nv.fused_blocks_per_lane(s, m, r, f) for _, s in TIERS
+            for (m, r, f) in (("four_over_six", "mse", False), ("rtn6", "mse", True),
+                              ("four_over_six", "mae", True))}
+    assert {1, 4, 12, 28} <= seen, seen
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+@pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
+def test_fused_edge_cases(nv, orc, name, mode, rule):
+    for fq in (False, True):
+        assert_matches_oracle(orc, EDGE[name], run_fused(nv, EDGE[name], mode, rule, fq),
+                              mode, rule, fq, name)
+
+
+def test_fused_poison_only_its_tensor(nv, orc):
+    x = W.bits(W.generate("moe", (4, 40, 160))).copy()
+    x[2, 7, 33] = 0x7FC0             # NaN
+    x[0, 0, 0] = 0xFF80              # -inf
+    for mode, rule in RUNS:
+        for fq in (False, True):
+            got = run_fused(nv, x, mode, rule, fq)
+            assert_matches_oracle(orc, x, got, mode, rule, fq, "poison")
+            assert np.isnan(got["alpha"][[0, 2]]).all() and np.isfinite(got["alpha"][[1, 3]]).all()
+
+
+@pytest.mark.parametrize("limit", [0, 1], ids=["never-wait", "one-poll"])
+@pytest.mark.parametrize("shape", [(5, 130, 320), (1024, 8208), (4096, 8448)],
+                         ids=["batched", "tier4", "tier12"])
+def test_fused_bounded_wait_fallback(nv, orc, limit, shape):
+    """The wait for the other workgroups is cut short from the host: workgroups that stop
+    waiting compute the tensor amax alone, and the result does not change."""
+    x = W.bits(W.weight(shape, seed=400))
+    nv.set_fused_wait_limit(limit)
+    try:
+        say("[fused] wait limit %d %s" % (limit, shape))
+        for mode, rule, fq in (("four_over_six", "mse", False), ("rtn6", "mse", True)):
+            assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq,
+                                  "limit%d" % limit)
+    finally:
+        nv.set_fused_wait_limit(-1)
+
+
+def test_fused_two_pass_route(nv, orc):
+    """A tensor too large to hold on chip, and in-place fake-quant, take the two-pass path."""
+    shape = (4096, 16384)                                  # 4.2 M blocks
+    assert nv.fused_blocks_per_lane(shape, "four_over_six", "mse", False) == 0
+    x = W.bits(W.weight(shape, seed=500))
+    got = run_fused(nv, x, "four_over_six", "mse", False)
+    assert_matches_oracle(orc, x, got, "four_over_six", "mse", False, "too-large")
+    xs = W.bits(W.generate("act", (64, 512)))
+    xg = to_gpu(xs)
+    y, al = nv.fakequant_fused(xg, "four_over_six", "mae", out=xg)
+    torch.cuda.synchronize()
+    ref = orc.quantize(xs, "four_over_six", "mae", want_y=True)
+    assert np.array_equal(u16(y), ref["y"])
+
+
+def test_fused_workspace_content_and_reuse(nv, orc):
+    """The workspace may hold anything before a call; one workspace serves consecutive calls
+    on a stream, and a larger one than needed is fine."""
+    ws = torch.full((8 * nv.FUSED_WS_WORDS,), -1, dtype=torch.int32, device="cuda")
+    for k, (name, shape) in enumerate(SMALL):
+        x = W.bits(W.generate(name, shape))
+        mode, rule = RUNS[k % 4]
+        for fq in (False, True):
+            assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq, workspace=ws),
+                                  mode, rule, fq, name)

@@ -51,18 +51,24 @@ def test_graph_replays_match_eager(nv, orc, shape, mode, rule):
     alpha_y = torch.empty(E, dtype=torch.float32, device="cuda")
     am = torch.empty(E, dtype=torch.float32, device="cuda")
     codes2, scales2, alpha2 = torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(alpha)
+    codes3, scales3, alpha3 = torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(alpha)
+    y3, alpha_y3 = torch.empty_like(x), torch.empty_like(alpha)
+    ws = torch.empty(nv.FUSED_WS_WORDS * E, dtype=torch.int32, device="cuda")
 
     def work():
         nv.quantize(x, mode, rule, codes=codes, scales=scales, alpha=alpha)
         nv.fakequant(x, mode, rule, out=y, alpha=alpha_y)
         nv.amax(x, out=am)
         nv.quantize_from_amax(x, am, mode, rule, codes=codes2, scales=scales2, alpha=alpha2)
+        nv.quantize_fused(x, mode, rule, codes=codes3, scales=scales3, alpha=alpha3, workspace=ws)
+        nv.fakequant_fused(x, mode, rule, out=y3, alpha=alpha_y3, workspace=ws)
 
     work()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (codes, scales, alpha, y, alpha_y, am, codes2, scales2, alpha2)]
+    outs = (codes, scales, alpha, y, alpha_y, am, codes2, scales2, alpha2, codes3, scales3,
+            alpha3, y3, alpha_y3)
+    ref = [t.clone() for t in outs]
     g = _capture(work)
-    outs = (codes, scales, alpha, y, alpha_y, am, codes2, scales2, alpha2)
     for r in range(4):
         for t in outs:
             t.zero_()
@@ -77,3 +83,4 @@ def test_graph_replays_match_eager(nv, orc, shape, mode, rule):
     o = orc.quantize(xb, mode, rule)
     assert np.array_equal(codes.cpu().numpy(), o["codes"])
     assert np.array_equal(W.bits(y.cpu()), o["y"])
+    assert torch.equal(codes3, codes) and torch.equal(y3, y) and torch.equal(alpha3, alpha)
