@@ -4,10 +4,15 @@ Flags that the arithmetic depends on:
   -ffp-contract=off      no fused multiply-add except where the source writes fma
   -packed-fp32-ops off   no v_pk_{add,mul,fma}_f32 generated for this code
   (defaults kept)        correctly rounded fp32 division, fp32 denormals preserved
+
+The build also reads the compiler's per-kernel resource report and fails if any kernel
+spills to scratch memory: the single-read kernel keeps up to 28 blocks per lane in
+registers at the 256-VGPR limit, and a spill there would be slow without being wrong.
 """
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 
@@ -33,15 +38,33 @@ def flags() -> list:
             "-fvisibility=hidden", "-Wall", "-I" + INCLUDE]
 
 
+def scratch_users(report: str) -> list:
+    """Kernels with a nonzero ScratchSize in a -Rpass-analysis=kernel-resource-usage report."""
+    users, name = [], None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            users.append((name, int(m.group(1))))
+    return users
+
+
 def build_library(verbose: bool = False) -> str:
     """Compile the kernels and the C ABI into LIB (atomically replaced)."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + flags() + ["-o", tmp, SRC]
+    cmd = [hipcc()] + flags() + ["-Rpass-analysis=kernel-resource-usage", "-o", tmp, SRC]
     res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
+    lines = (res.stdout + res.stderr).splitlines()
+    out = "\n".join(l for l in lines
+                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + out)
+    spills = scratch_users("\n".join(lines))
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError("kernels spill to scratch memory: %s" % spills)
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)

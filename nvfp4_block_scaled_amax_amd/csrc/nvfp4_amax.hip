@@ -432,6 +432,17 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// Packed outputs (8 code bytes, 1 scale byte per block) are written as non-temporal
+// (streaming) stores: they are not read again by this kernel, and measured 2-4 % faster on
+// the block pass than write-back stores (the fake-quant output, whole 32-byte blocks, is
+// not, and keeps ordinary stores).
+__device__ __forceinline__ void store_packed(char* codesT, uint8_t* scalesT, uint32_t u,
+                                             uint32_t w0, uint32_t w1, uint32_t sc) {
+  typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u2v{w0, w1}, reinterpret_cast<u2v*>(codesT + (u << 3)));
+  __builtin_nontemporal_store((uint8_t)sc, scalesT + u);
+}
+
 __device__ __forceinline__ void unpack16(const uint4& p0, const uint4& p1, float (&x)[16]) {
   const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
@@ -544,8 +555,7 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
       *reinterpret_cast<uint4*>(outT + (u << 5)) = make_uint4(y[0], y[1], y[2], y[3]);
       *reinterpret_cast<uint4*>(outT + (u << 5) + 16) = make_uint4(y[4], y[5], y[6], y[7]);
     } else {
-      *reinterpret_cast<uint2*>(codesT + (u << 3)) = make_uint2(w0, w1);
-      scalesT[u] = (uint8_t)sc;
+      store_packed(codesT, scalesT, u, w0, w1, sc);
       if (DIAG) {
         qstar[base + u] = four ? 4 : 6;
         n_four += four ? 1u : 0u;
@@ -682,8 +692,7 @@ __device__ __forceinline__ void fused_emit(const uint4& c0, const uint4& c1, uin
     *reinterpret_cast<uint4*>(outT + (u << 5)) = make_uint4(y[0], y[1], y[2], y[3]);
     *reinterpret_cast<uint4*>(outT + (u << 5) + 16) = make_uint4(y[4], y[5], y[6], y[7]);
   } else {
-    *reinterpret_cast<uint2*>(codesT + (u << 3)) = make_uint2(w0, w1);
-    scalesT[u] = (uint8_t)sc;
+    store_packed(codesT, scalesT, u, w0, w1, sc);
   }
 }
 

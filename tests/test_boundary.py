@@ -174,3 +174,14 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), fn
                 assert "nvfp4_oracle" not in text, fn
+
+
+def test_build_rejects_kernels_that_spill():
+    from nvfp4_block_scaled_amax_amd import build
+    report = "\n".join([
+        "k.hip:1:1: remark: Function Name: a_kernel [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark: Function Name: b_kernel [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark:     ScratchSize [bytes/lane]: 24 [-Rpass-analysis=kernel-resource-usage]"])
+    assert build.scratch_users(report) == [("b_kernel", 24)]
+    assert build.scratch_users(report.replace(": 24 ", ": 0 ")) == []
