@@ -82,7 +82,8 @@ def main():
                          "skip the CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path; a tensor "
+              "would be sharded by rows with one all-reduce(MAX) of its amax "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
