@@ -11,8 +11,8 @@
 //                    values), reduced per wavefront with DPP row moves and per workgroup in
 //                    LDS, then one atomicMax per workgroup on the tensor's float bits
 //   quantize_kernel  one lane owns whole 16-element blocks: both candidate scales, the FP4
-//                    rounding, the error reduction and the selection stay in VGPRs; codes,
-//                    scale bytes (or bf16 fake-quant values) are written with vector stores
+//                    rounding, the error reduction and the selection stay in VGPRs; codes
+//                    and scale bytes (or bf16 fake-quant values) leave in streaming stores
 //   alpha_kernel     alpha[e] <- amax[e] / (6*M) once every block is done
 //   (the diagnostics variant of quantize_kernel also reduces per-tensor error statistics
 //   in binary64 and adds them with one atomic per field per workgroup)
@@ -20,10 +20,11 @@
 //                    and keeps each lane's blocks (VGPRs + LDS), reduces amax, waits for
 //                    every workgroup of the tensor at a grid-wide counter, then runs the
 //                    block pass on the blocks it holds
+//   dequant_kernel   packed codes + scale bytes + alpha -> bf16, one block per lane
 //
-// All floating-point steps are IEEE binary32 with round-to-nearest-even, no contraction
-// (-ffp-contract=off) and no denormal flushing; fp32 division and reciprocal are the
-// correctly rounded HIP defaults.
+// All floating-point steps of the encoding are IEEE binary32 with round-to-nearest-even, no
+// contraction (-ffp-contract=off) and no denormal flushing; fp32 division and reciprocal are
+// the correctly rounded HIP defaults.  (Only the diagnostics' error sums are binary64.)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -638,21 +639,23 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 // (the same exact value), so every wave exits whatever the scheduling.
 //
 // Workspace of one tensor (kFusedWsWords words, zeroed before the launch), one 128-byte line
-// per group so that arrivals and polls spread over many lines: workgroup g belongs to group
-// g % S (S = min(16, G)); line i holds the group's max (atomicMax), arrival count and ready
-// flag; the top line holds the max and count over the groups.  The workgroup that completes a
-// group forwards the group max to the top line; the one that completes the top line writes
-// (amax | 1) into every group's flag (amax bits have 16 zero low bits), so a poller needs
-// nothing else from memory.  All of it is relaxed device-scope atomics: an acquire or release
-// at device scope writes back and invalidates the L2 of the XCD, which at a thousand
-// workgroups cost more than 100 us.  With at least 8 workgroups per group and at most 16
-// groups, a launch of fewer than 16 workgroups uses one group and no top level.  The one
-// ordering needed -- a workgroup's max is performed
-// before its count -- comes from issuing the count only after the returning atomicMax is back
-// (a register dependency on its result); a group's completer reads the group max only after
-// its own count returned, so every member's max is in.
+// per group so that arrivals and polls spread over many lines.  Workgroup g belongs to group
+// g % S, with S = min(16, max(1, G / 8)) groups of at least 8 workgroups; line i holds the
+// group's max (atomicMax), arrival count and ready flag, and the top line the max and count
+// over the groups.  The workgroup that completes a group forwards the group max to the top
+// line; the one that completes the top line writes (amax | 1) into every group's flag (amax
+// bits have 16 zero low bits), so a poller needs nothing else from memory.  With one group
+// (fewer than 16 workgroups) its completer publishes directly.
+//
+// All of it is relaxed device-scope atomics: an acquire or release at device scope writes
+// back and invalidates the L2 of the XCD, which at a thousand workgroups cost more than
+// 100 us.  The one ordering needed, a workgroup's max performed before its count, comes from
+// issuing the count only after the returning atomicMax is back (a register dependency on its
+// result).  A group's completer reads the group max only after its own count returned, so
+// every member's max is in; the top level works the same way.
 constexpr uint32_t kFusedDefaultWaitLimit = 1u << 20;   // polls of ~1 us (a device-scope load
                                                          // and a short sleep): about 1 s
+constexpr uint32_t kFusedMaxWaitLimit = 1u << 26;       // the most a caller may set: ~1 min
 constexpr int kFusedGroups = 16;
 constexpr int kLineWords = 32;                           // 128 bytes
 constexpr int64_t kFusedWsWords = (kFusedGroups + 1) * kLineWords;
@@ -1356,6 +1359,6 @@ NVFP4_EXPORT int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols,
 
 NVFP4_EXPORT void nvfp4_fused_set_wait_limit(int64_t polls) {
   g_wait_limit.store(polls < 0 ? kFusedDefaultWaitLimit
-                               : (uint32_t)std::min<int64_t>(polls, 0xFFFFFFFFll),
+                               : (uint32_t)std::min<int64_t>(polls, kFusedMaxWaitLimit),
                      std::memory_order_relaxed);
 }
