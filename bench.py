@@ -18,7 +18,10 @@ Timing:
     (2 B/elem amax read + 2.5625 B/elem block pass, or 4 B/elem fake-quant).
   * per-kernel legs: graphs of back-to-back launches of one pass over rotating
     cold buffers, HIP events recorded on the launch stream before and after the
-    replay; the average launch of the block pass is the roofline figure.
+    replay; the average launch of the block pass is the roofline figure.  Also
+    timed this way: the rtn6 block pass, the amax pass, the two-pass and the
+    single-read dynamic calls, the diagnostics call (with and without error
+    statistics) and dequantize (packed -> bf16).
 Printed: one JSON line.
 """
 from __future__ import annotations
@@ -40,6 +43,7 @@ MALL_BYTES = 256 << 20          # Infinity Cache
 AMAX_BPE = 2.0                  # bytes per element: bf16 read
 PACKED_BPE = 2.0 + 0.5 + 1.0 / 16   # bf16 read + 4-bit code + 1 scale byte per 16
 FQ_BPE = 4.0                    # bf16 read + bf16 write
+DEQUANT_BPE = 0.5 + 1.0 / 16 + 2.0   # 4-bit code + scale byte read, bf16 written
 KERNEL_SRC = os.path.join(ROOT, "nvfp4_block_scaled_amax_amd", "csrc", "nvfp4_amax.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "quantize_kernel_counters.txt")
 
@@ -141,6 +145,29 @@ def main():
                         alpha=alphas[i])
 
     ws = torch.empty(nv.FUSED_WS_WORDS * E, dtype=torch.int32, device=dev)
+    # packed inputs for the dequantize leg, and outputs for it and for the diagnostics leg
+    if fq:
+        pk = [(torch.empty(lead + (rows, cols // 2), dtype=torch.uint8, device=dev),
+               torch.empty(lead + (rows, cols // 16), dtype=torch.uint8, device=dev))
+              for _ in range(R)]
+        ys = outs
+    else:
+        pk = outs
+        ys = [torch.empty_like(xs[0]) for _ in range(R)]
+    qstar = [torch.empty_like(pk[0][1]) for _ in range(R)]
+    count4 = torch.empty(E, dtype=torch.int32, device=dev)
+    stats = torch.empty((E, len(nv.STATS)), dtype=torch.float64, device=dev)
+
+    def dequant_call(i):
+        nv.dequantize(pk[i][0], pk[i][1], alphas[i], out=ys[i])
+
+    def diag_call(i, with_stats):
+        st = nv.lib().nvfp4_quantize_diag(
+            xs[i].data_ptr(), E, rows, cols, 16, nv.MODES[args.mode], nv.RULES[args.rule],
+            pk[i][0].data_ptr(), pk[i][1].data_ptr(), alphas[i].data_ptr(),
+            qstar[i].data_ptr(), count4.data_ptr(), stats.data_ptr() if with_stats else None,
+            torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
 
     def fused_call(i):
         if fq:
@@ -197,6 +224,9 @@ def main():
     B = max(4 * R, 32)
     for i in range(R):
         amax_pass(i)
+        if fq:      # packed codes of the same tensor for the dequantize leg
+            nv.quantize_from_amax(xs[i], amaxs[i], args.mode, args.rule, codes=pk[i][0],
+                                  scales=pk[i][1], alpha=alphas[i])
     torch.cuda.synchronize()
     legs = {}
     for name, fn in (("block", block_pass),
@@ -204,7 +234,10 @@ def main():
                      ("block_again", block_pass),          # 4/6 once more: drift check
                      ("amax", amax_pass),
                      ("dynamic_entry_point", dynamic_call),
-                     ("fused_entry_point", fused_call)):
+                     ("fused_entry_point", fused_call),
+                     ("diagnostics", lambda i: diag_call(i, False)),
+                     ("diagnostics_with_stats", lambda i: diag_call(i, True)),
+                     ("dequantize", dequant_call)):
         g = capture(fn, B)
         legs[name] = replay_avg_us(g, B)
         del g
@@ -245,6 +278,10 @@ def main():
                 "GBps": round(pass_bpe * N / (legs["fused_entry_point"] * 1e-6) / 1e9, 1),
                 "speedup_vs_dynamic": round(legs["dynamic_entry_point"] /
                                             legs["fused_entry_point"], 3)},
+            "diagnostics": {"avg_us": round(legs["diagnostics"], 2),
+                            "with_stats_avg_us": round(legs["diagnostics_with_stats"], 2)},
+            "dequantize": {"avg_us": round(legs["dequantize"], 2),
+                           "GBps": round(DEQUANT_BPE * N / (legs["dequantize"] * 1e-6) / 1e9, 1)},
         },
         "overhead_4over6_vs_rtn6": round(t_block / t_rtn6 - 1.0, 4),
     }

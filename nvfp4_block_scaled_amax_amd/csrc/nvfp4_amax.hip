@@ -170,16 +170,19 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #ifndef NVFP4_WAVES_PER_EU
 #define NVFP4_WAVES_PER_EU 4         // occupancy floor: caps the block pass at 128 VGPRs
 #endif
-#ifndef NVFP4_BLOCK_WGS
-#define NVFP4_BLOCK_WGS 1024        // workgroups of the block pass over all tensors of a launch
-#endif
-// Launches of at least 2^23 blocks (268 MB of bf16 input and more) run on three 256-thread
-// workgroups per CU instead of four: measured 2-3 % faster than four on 470 MB and 1.3 GB
-// inputs, and 3-5 % slower on 67-117 MB inputs.
-#ifndef NVFP4_BLOCK_WGS_LONG
-#define NVFP4_BLOCK_WGS_LONG 768
-#endif
+// Grid of the block pass (grid-stride loop, the next block's loads issued before the current
+// block's arithmetic).  Measured on 67 MB to 1.3 GB inputs, same box, A/B:
+//   - rtn6 and fake-quant are light per block and run fastest with one block per lane and as
+//     many waves as fit: 5-17 % faster than a fixed 1024 workgroups.
+//   - Four Over Six into packed output (two trials per block) needs its own loads in flight
+//     across its arithmetic.  Below 2^23 blocks (268 MB of input) 1024 workgroups in all
+//     (about 14 blocks per lane for the 4096x14336 weight) beat 4 blocks per lane by 3-5 %;
+//     from 2^23 blocks on, 4 blocks per lane beat 1024 or 768 workgroups by 4-12 % (MoE 10 %).
+//   - The diagnostics variant ends with same-address atomics per workgroup: 1024 in all.
 constexpr int64_t kLongLaunchBlocks = INT64_C(1) << 23;
+constexpr int64_t kShortLaunchWGs = 1024;
+constexpr int64_t kLaneBlocksLong = 4;
+constexpr int64_t kDiagLaunchWGs = 1024;
 
 // Reference path for one candidate, straight from the definition, one binary32 step at a
 // time (correctly rounded division and reciprocal, threshold-count FP4 rounding).  The
@@ -856,6 +859,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // Dequantize: packed codes + scale bytes + alpha -> bf16, one block per lane per step.
 // d = RN(dec(s) * alpha) and y = bf16(RN(val(code) * d)): the values the fake-quant output
 // holds for the tensor that was quantized.  A NaN alpha or scale byte gives NaN (0x7FC0).
+// Grid and addressing as in quantize_kernel: x = workgroups per tensor, y = tensor, 32-bit
+// block indices, grid-stride with the next step's 9 bytes loaded before the current step's
+// arithmetic; launched with one block per lane.
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint2* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ alpha,
@@ -864,24 +870,35 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint2* __restri
   const float al = alpha[t];
   const bool nan_alpha = al != al;
   const int64_t base = t * nblk;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += stride) {
-    const uint2 c = codes[base + b];
-    const uint32_t sb = scales[base + b];
-    uint4 y0, y1;
+  const char* codesT = reinterpret_cast<const char*>(codes + base);   // 8 bytes per block
+  const uint8_t* scalesT = scales + base;
+  char* outT = reinterpret_cast<char*>(out + 2 * base);              // 32 bytes per block
+  const uint32_t n = (uint32_t)nblk;
+  const uint32_t stride = gridDim.x * kThreads;
+  uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  uint2 nc = make_uint2(0u, 0u);
+  uint32_t ns = 0u;
+  if (u < n) {
+    nc = *reinterpret_cast<const uint2*>(codesT + (u << 3));
+    ns = scalesT[u];
+  }
+  for (; u < n; u += stride) {
+    const uint2 c = nc;
+    const uint32_t sb = ns;
+    const uint32_t un = min(u + stride, n - 1);   // always in bounds: reloads the last block
+    nc = *reinterpret_cast<const uint2*>(codesT + (un << 3));
+    ns = scalesT[un];
+    uint32_t y[8];
     if (nan_alpha || (sb & 0x7Fu) == 0x7Fu) {
-      y0 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
-      y1 = y0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = 0x7FC07FC0u;
     } else {
       const float dec = e4m3_to_f32(sb & 0x7Fu);
-      const float d = (sb & 0x80u ? -dec : dec) * al;
-      uint32_t y[8];
-      dequant_bf16(c.x, c.y, d, y);
-      y0 = make_uint4(y[0], y[1], y[2], y[3]);
-      y1 = make_uint4(y[4], y[5], y[6], y[7]);
+      dequant_bf16(c.x, c.y, (sb & 0x80u ? -dec : dec) * al, y);
     }
-    out[2 * (base + b)] = y0;
-    out[2 * (base + b) + 1] = y1;
+    // ordinary stores: streaming ones measured 20 % slower here (a write-only stream)
+    *reinterpret_cast<uint4*>(outT + (u << 5)) = make_uint4(y[0], y[1], y[2], y[3]);
+    *reinterpret_cast<uint4*>(outT + (u << 5) + 16) = make_uint4(y[4], y[5], y[6], y[7]);
   }
 }
 
@@ -950,9 +967,14 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
                        uint8_t* scales, uint16_t* out, float* alpha_out, uint8_t* qstar,
                        uint32_t* count4, double* stats, hipStream_t stream) {
   auto launch = [&](int64_t E, int64_t nblk, int64_t first_tensor, int64_t first_block) {
-    const int64_t want = (nblk + kThreads - 1) / kThreads;
-    const int64_t wgs = E * nblk >= kLongLaunchBlocks ? NVFP4_BLOCK_WGS_LONG : NVFP4_BLOCK_WGS;
-    const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, wgs / E));
+    const int64_t one_per_lane = (nblk + kThreads - 1) / kThreads;
+    int64_t per_tensor = one_per_lane;
+    if (DIAG)
+      per_tensor = std::min(one_per_lane, std::max<int64_t>(1, kDiagLaunchWGs / E));
+    else if (MODE == NVFP4_FOUR_OVER_SIX && !FQ)
+      per_tensor = E * nblk < kLongLaunchBlocks
+                       ? std::min(one_per_lane, std::max<int64_t>(1, kShortLaunchWGs / E))
+                       : (nblk + kThreads * kLaneBlocksLong - 1) / (kThreads * kLaneBlocksLong);
     const int64_t b0 = first_tensor * s.nblk + first_block;   // first block of this launch
     hipLaunchKernelGGL((quantize_kernel<MODE, RULE, FQ, DIAG>),
                        dim3((unsigned)per_tensor, (unsigned)E), dim3(kThreads), 0, stream,
@@ -1256,11 +1278,21 @@ NVFP4_EXPORT nvfp4_status nvfp4_dequantize(const uint8_t* codes, const uint8_t* 
       overlap(out, out_bytes, alpha, s.E * 4))
     return NVFP4_ERR_ALIAS;
   (void)hipGetLastError();
-  const int64_t want = (s.nblk + kThreads - 1) / kThreads;
-  const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(want, NVFP4_BLOCK_WGS / s.E));
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kThreads), 0,
-                     stream, reinterpret_cast<const uint2*>(codes), scales, alpha, s.nblk,
-                     reinterpret_cast<uint4*>(out));
+  auto launch = [&](int64_t E2, int64_t nblk, int64_t first_tensor, int64_t first_block) {
+    // one block per lane (measured 12-30 % faster than 1024 workgroups striding the tensor)
+    const int64_t per_tensor = std::max<int64_t>(1, (nblk + kThreads - 1) / kThreads);
+    const int64_t b0 = first_tensor * s.nblk + first_block;
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)per_tensor, (unsigned)E2), dim3(kThreads), 0,
+                       stream, reinterpret_cast<const uint2*>(codes + b0 * 8), scales + b0,
+                       alpha + first_tensor, nblk, reinterpret_cast<uint4*>(out + b0 * 16));
+  };
+  if (s.nblk <= kMaxLaunchBlocks) {
+    launch(s.E, s.nblk, 0, 0);
+  } else {                  // tensors of 2^27 blocks or more: one launch per tensor and chunk
+    for (int64_t t = 0; t < s.E; ++t)
+      for (int64_t b = 0; b < s.nblk; b += kMaxLaunchBlocks)
+        launch(1, std::min(kMaxLaunchBlocks, s.nblk - b), t, b);
+  }
   return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

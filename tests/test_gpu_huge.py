@@ -4,8 +4,8 @@ Block indices inside a kernel are 32-bit, so the host splits the block pass of a
 2^27 blocks or more into launches over consecutive block ranges (offset pointers, one tensor
 per launch).  This runs the dynamic packed, fake-quant and diagnostics calls on a
 131080 x 16384 bf16 tensor (2^27 + 8192 blocks, 4.3 GB) and compares the whole packed output,
-alpha, the count of blocks scaled to 4, and sampled fake-quant blocks around the launch
-boundary with the oracle."""
+alpha, the count of blocks scaled to 4, and sampled fake-quant and dequantized blocks around
+the launch boundary with the oracle (dequantize splits its launches the same way)."""
 from __future__ import annotations
 
 import os
@@ -53,7 +53,20 @@ def test_tensor_over_2pow27_blocks(nv, orc):
     assert torch.equal(cq, c) and torch.equal(sq, s) and torch.equal(aq, a)
     codes, scales = c.cpu().numpy(), s.cpu().numpy()
     qstar_gpu, n4_gpu = q.cpu().numpy(), int(n4.cpu()[0])
-    del c, s, cq, sq, q
+    del cq, sq, q
+
+    say("[huge] dequantize, sampled around the launch boundary")
+    rng = np.random.default_rng(78)
+    ids = np.unique(np.concatenate([rng.integers(0, NBLK, size=20000),
+                                    np.arange(SPLIT - 512, SPLIT + 512),
+                                    np.arange(NBLK - 256, NBLK), np.arange(256)]))
+    ydq = nv.dequantize(c, s, a)
+    torch.cuda.synchronize()
+    got = ydq.view(-1, 16)[torch.from_numpy(ids).cuda()].cpu().view(torch.int16).numpy()
+    want = orc.dequantize(codes.reshape(-1, 8)[ids].reshape(1, -1, 8),
+                          scales.reshape(-1)[ids].reshape(1, -1, 1), a.cpu().numpy())
+    assert np.array_equal(got.view(np.uint16).reshape(-1), want.reshape(-1))
+    del c, s, ydq
 
     say("[huge] oracle, whole tensor")
     ref = orc.quantize(x, "four_over_six", "mse", nthreads=NTHREADS, want_y=False,
@@ -68,10 +81,6 @@ def test_tensor_over_2pow27_blocks(nv, orc):
     say("[huge] fake-quant, rtn6, sampled around the launch boundary")
     y, a2 = nv.fakequant(xg, "rtn6", "mse")
     torch.cuda.synchronize()
-    rng = np.random.default_rng(78)
-    ids = np.unique(np.concatenate([rng.integers(0, NBLK, size=20000),
-                                    np.arange(SPLIT - 512, SPLIT + 512),
-                                    np.arange(NBLK - 256, NBLK), np.arange(256)]))
     yb = y.view(-1, 16)[torch.from_numpy(ids).cuda()].cpu().view(torch.int16).numpy()
     al = np.array([orc.alpha(float(orc.amax(x, 1)[0]), "rtn6")], np.float32)
     assert np.array_equal(a2.cpu().numpy().view(np.uint32), al.view(np.uint32))
