@@ -157,6 +157,7 @@ def main():
     qstar = [torch.empty_like(pk[0][1]) for _ in range(R)]
     count4 = torch.empty(E, dtype=torch.int32, device=dev)
     stats = torch.empty((E, len(nv.STATS)), dtype=torch.float64, device=dev)
+    stats_ws = torch.empty(nv.diag_ws_words(E), dtype=torch.int32, device=dev)
 
     def dequant_call(i):
         nv.dequantize(pk[i][0], pk[i][1], alphas[i], out=ys[i])
@@ -166,7 +167,7 @@ def main():
             xs[i].data_ptr(), E, rows, cols, 16, nv.MODES[args.mode], nv.RULES[args.rule],
             pk[i][0].data_ptr(), pk[i][1].data_ptr(), alphas[i].data_ptr(),
             qstar[i].data_ptr(), count4.data_ptr(), stats.data_ptr() if with_stats else None,
-            torch.cuda.current_stream().cuda_stream)
+            stats_ws.data_ptr() if with_stats else None, torch.cuda.current_stream().cuda_stream)
         assert st == 0, st
 
     def fused_call(i):

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 3
+#define NVFP4_ABI_VERSION 4
 #define NVFP4_BLOCK 16
 
 typedef enum { NVFP4_RTN6 = 0, NVFP4_FOUR_OVER_SIX = 1 } nvfp4_mode;
@@ -153,19 +153,28 @@ enum {
  *   - per tensor, the number of blocks scaled to 4 (out_count4 [E], cleared by the call);
  *   - optionally (out_stats may be NULL), per tensor, the error statistics NVFP4_STAT_*
  *     (out_stats [E][6] binary64, 8-byte aligned, cleared by the call; NaN for a poisoned
- *     tensor).
+ *     tensor).  They need stats_workspace: device memory of NVFP4_DIAG_WS_WORDS(E) uint32,
+ *     128-byte aligned, owned by the caller, any content (the call clears what it uses),
+ *     not shared with a call that may overlap this one; ignored (may be NULL) without
+ *     out_stats.  Each workgroup leaves its partial sums there, and the last one of each
+ *     tensor adds them up.
  * The Four Over Six explainer expects blocks with large near-max values to pick 4 ("Key
  * contributions and results"), and reports that rounding the block scales to FP8 costs
  * little while rounding the values between 66.6 % and 100 % of the block max drives the
  * error ("Problem definition"): out_count4, NVFP4_STAT_SSE_NEAR and the gap between
  * NVFP4_STAT_SSE and NVFP4_STAT_SSE_F32SCALE measure these on a given tensor.  The maximum
- * and the count are exact; the sums are binary64 with an order that depends on the launch,
- * within (n - 1) * 2^-53 of the exact sum relative to it (n = elements per tensor). */
+ * and the count are exact; the sums are binary64, within (n - 1) * 2^-53 of the exact sum
+ * relative to it (n = elements per tensor), and their summation order is fixed by the shape
+ * alone, so repeated calls give the same bits.  Errors as for the other calls, plus
+ * NVFP4_ERR_NULL for a null qstar, count4 or (with out_stats) stats_workspace,
+ * NVFP4_ERR_ALIGN and NVFP4_ERR_ALIAS for those arrays. */
+#define NVFP4_DIAG_WS_WORDS(E) \
+  (32 * (int64_t)(E) + 12 * ((int64_t)(E) > 1024 ? (int64_t)(E) : (int64_t)1024))
 nvfp4_status nvfp4_quantize_diag(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
                                  int block, nvfp4_mode mode, nvfp4_rule rule,
                                  uint8_t* out_codes, uint8_t* out_scales, float* out_alpha,
                                  uint8_t* out_qstar, uint32_t* out_count4, double* out_stats,
-                                 hipStream_t stream);
+                                 uint32_t* stats_workspace, hipStream_t stream);
 
 /* Single-read dynamic quantization: the outputs of nvfp4_quantize_batched /
  * nvfp4_fakequant_batched, bit for bit, reading the input from HBM once instead of twice.

@@ -37,8 +37,15 @@ class NVFP4Error(RuntimeError):
 
 
 _lib = None
-ABI_VERSION = 3                  # NVFP4_ABI_VERSION of include/nvfp4_amax.h
+ABI_VERSION = 4                  # NVFP4_ABI_VERSION of include/nvfp4_amax.h
 FUSED_WS_WORDS = 544             # NVFP4_FUSED_WS_WORDS: workspace int32 words per tensor
+
+
+def diag_ws_words(E: int) -> int:
+    """NVFP4_DIAG_WS_WORDS(E): int32 words of quantize_diag's statistics workspace."""
+    return 32 * E + 12 * max(E, 1024)
+
+
 # Columns of the per-tensor statistics of quantize_diag (NVFP4_STAT_* order).
 STATS = ("sse", "sae", "maxerr", "sse_near", "sse_f32scale", "near_count")
 
@@ -65,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P]
         L.nvfp4_fakequant_from_amax.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
         L.nvfp4_dequantize.argtypes = [P, P, P, i64, i64, i64, P, P]
-        L.nvfp4_quantize_diag.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P]
+        L.nvfp4_quantize_diag.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.nvfp4_quantize_fused.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P]
         L.nvfp4_fakequant_fused.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
         L.nvfp4_fused_single_read.argtypes = [i64, i64, i64, i32, i32, i32]
@@ -156,19 +163,25 @@ def quantize(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=None, s
     return codes, scales, alpha
 
 
-def quantize_diag(x: torch.Tensor, mode="four_over_six", rule="mse", *, stats=True):
+def quantize_diag(x: torch.Tensor, mode="four_over_six", rule="mse", *, stats=True,
+                  workspace=None):
     """Packed NVFP4 (dynamic scale) plus diagnostics ->
     (codes, scales, alpha, qstar, count4, stats): qstar uint8 [..., rows, cols/16] is 4 or 6
     per block, count4 int32 [E] counts the blocks scaled to 4, and stats float64 [E, 6]
-    (columns STATS; None when stats=False) holds per-tensor error statistics."""
+    (columns STATS; None when stats=False) holds per-tensor error statistics.  workspace:
+    int32 [diag_ws_words(E)], 128-byte aligned, for the statistics (allocated here if None)."""
     E, rows, cols, batched = _dims(x)
     codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, None, None, None)
     qstar = torch.empty_like(scales)
     count4 = torch.empty(E, dtype=torch.int32, device=x.device)
-    st_out = torch.empty((E, len(STATS)), dtype=torch.float64, device=x.device) if stats else None
+    st_out = ws = None
+    if stats:
+        st_out = torch.empty((E, len(STATS)), dtype=torch.float64, device=x.device)
+        ws = _workspace(workspace, diag_ws_words(E), x)
     st = lib().nvfp4_quantize_diag(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
                                    _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(qstar),
-                                   _ptr(count4), _ptr(st_out) if stats else None, _stream(x))
+                                   _ptr(count4), _ptr(st_out) if stats else None,
+                                   _ptr(ws) if stats else None, _stream(x))
     _check(st, "nvfp4_quantize_diag")
     return codes, scales, alpha, qstar, count4, st_out
 
@@ -237,13 +250,13 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, *
 
 
 # ----------------------------------------------------------------------------- single read
-def _workspace(workspace, E, x):
+def _workspace(workspace, words, x):
     if workspace is None:
-        return torch.empty(FUSED_WS_WORDS * E, dtype=torch.int32, device=x.device)
+        return torch.empty(words, dtype=torch.int32, device=x.device)
     if (workspace.device != x.device or workspace.dtype not in (torch.int32, torch.uint32)
-            or workspace.numel() < FUSED_WS_WORDS * E or not workspace.is_contiguous()):
-        raise ValueError("workspace must be a contiguous int32 tensor of %d*E elements on x's "
-                         "device" % FUSED_WS_WORDS)
+            or workspace.numel() < words or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous int32 tensor of at least %d elements "
+                         "on x's device" % words)
     return workspace
 
 
@@ -254,7 +267,7 @@ def quantize_fused(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=N
     aligned (allocated here if None)."""
     E, rows, cols, batched = _dims(x)
     codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha)
-    ws = _workspace(workspace, E, x)
+    ws = _workspace(workspace, FUSED_WS_WORDS * E, x)
     st = lib().nvfp4_quantize_fused(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
                                     _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(ws), _stream(x))
     _check(st, "nvfp4_quantize_fused")
@@ -268,7 +281,7 @@ def fakequant_fused(x: torch.Tensor, mode="four_over_six", rule="mse", *, out=No
     E, rows, cols, batched = _dims(x)
     out = _out(out, x.shape, torch.bfloat16, x)
     alpha = _out(alpha, (E,), torch.float32, x)
-    ws = _workspace(workspace, E, x)
+    ws = _workspace(workspace, FUSED_WS_WORDS * E, x)
     st = lib().nvfp4_fakequant_fused(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
                                      _ptr(out), _ptr(alpha), _ptr(ws), _stream(x))
     _check(st, "nvfp4_fakequant_fused")

@@ -57,8 +57,16 @@ def build_library(verbose: bool = False) -> str:
     cmd = [hipcc()] + flags() + ["-Rpass-analysis=kernel-resource-usage", "-o", tmp, SRC]
     res = subprocess.run(cmd, capture_output=True, text=True)
     lines = (res.stdout + res.stderr).splitlines()
-    out = "\n".join(l for l in lines
-                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
+    kept, skip = [], 0
+    for l in lines:              # drop the resource remarks with their source-line context
+        if "kernel-resource-usage" in l:
+            skip = 2
+        elif skip and re.match(r"^\s*\d*\s*\|", l):
+            skip -= 1
+        elif "packed-fp32-ops" not in l:
+            skip = 0
+            kept.append(l)
+    out = "\n".join(kept)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + out)
     spills = scratch_users("\n".join(lines))

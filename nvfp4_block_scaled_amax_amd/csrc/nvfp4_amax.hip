@@ -15,7 +15,8 @@
 //                    and scale bytes (or bf16 fake-quant values) leave in streaming stores
 //   alpha_kernel     alpha[e] <- amax[e] / (6*M) once every block is done
 //   (the diagnostics variant of quantize_kernel also reduces per-tensor error statistics
-//   in binary64 and adds them with one atomic per field per workgroup)
+//   in binary64: each workgroup leaves its partial sums in a slot of the caller's
+//   workspace, and the last to arrive sums the slots in a fixed order)
 //   fused_kernel     single-read dynamic quantization for tensors that fit on chip: loads
 //                    and keeps each lane's blocks (VGPRs + LDS), reduces amax, waits for
 //                    every workgroup of the tensor at a grid-wide counter, then runs the
@@ -80,13 +81,15 @@ __device__ __forceinline__ float e2m1_value_of(uint32_t m) {
 
 // ----------------------------------------------------------------------------- kernels
 __global__ void clear_kernel(uint32_t* __restrict__ acc, uint32_t* __restrict__ acc2, int64_t E,
-                             uint32_t* __restrict__ acc3, int64_t n3) {
+                             uint32_t* __restrict__ acc3, int64_t n3, uint32_t* __restrict__ acc4,
+                             int64_t n4) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < E) {
     acc[i] = 0u;
     if (acc2) acc2[i] = 0u;
   }
   if (acc3 && i < n3) acc3[i] = 0u;
+  if (acc4 && i < n4) acc4[i] = 0u;
 }
 
 // Max of two packed unsigned 16-bit lanes (v_pk_max_u16).
@@ -178,11 +181,18 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //     across its arithmetic.  Below 2^23 blocks (268 MB of input) 1024 workgroups in all
 //     (about 14 blocks per lane for the 4096x14336 weight) beat 4 blocks per lane by 3-5 %;
 //     from 2^23 blocks on, 4 blocks per lane beat 1024 or 768 workgroups by 4-12 % (MoE 10 %).
-//   - The diagnostics variant ends with same-address atomics per workgroup: 1024 in all.
+//   - The diagnostics variant ends with one or two same-address atomics per workgroup (the
+//     count of blocks scaled to 4, the statistics counter): 1024 workgroups in all.
 constexpr int64_t kLongLaunchBlocks = INT64_C(1) << 23;
 constexpr int64_t kShortLaunchWGs = 1024;
 constexpr int64_t kLaneBlocksLong = 4;
 constexpr int64_t kDiagLaunchWGs = 1024;
+constexpr int kDiagCtrWords = 32;        // statistics workspace: one 128-byte counter line per tensor
+constexpr int kDiagSlot = NVFP4_NSTATS;  // and six binary64 partials per workgroup
+static_assert(NVFP4_DIAG_WS_WORDS(1) == kDiagCtrWords + 2 * kDiagSlot * kDiagLaunchWGs &&
+                  NVFP4_DIAG_WS_WORDS(2048) == 2048 * (kDiagCtrWords + 2 * kDiagSlot),
+              "statistics workspace size");
+using u64 = unsigned long long;
 
 // Reference path for one candidate, straight from the definition, one binary32 step at a
 // time (correctly rounded division and reciprocal, threshold-count FP4 rounding).  The
@@ -379,8 +389,12 @@ struct LaneStats {
   uint32_t near;
 };
 
+// The near-max test 3|x| > 2 bmax is taken as 1.5|x| > bmax in binary32: |x| is a bf16 value
+// (8 significant bits, exponent at least -133), so 1.5|x| is exact unless it overflows, and
+// an overflow means 1.5|x| exceeds every finite bmax, which the comparison with +inf also says.
+// Branch-free: the far elements add a zero to the near sum.
 template <int SEL>
-__device__ __forceinline__ void pair_stats(uint32_t w, float xa, float xb, float d, double thr,
+__device__ __forceinline__ void pair_stats(uint32_t w, float xa, float xb, float d, float bmax,
                                            LaneStats& st) {
   const f32x2 val = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);   // signed values
   const float ea = xa - val.x * d;
@@ -391,41 +405,61 @@ __device__ __forceinline__ void pair_stats(uint32_t w, float xa, float xb, float
   st.sae = st.sae + __builtin_fabs(da);
   st.sae = st.sae + __builtin_fabs(db);
   st.mx = max3_abs(st.mx, ea, eb);
-  if (3.0 * (double)fabsf(xa) > thr) { st.near_sse = __builtin_fma(da, da, st.near_sse); ++st.near; }
-  if (3.0 * (double)fabsf(xb) > thr) { st.near_sse = __builtin_fma(db, db, st.near_sse); ++st.near; }
+  const bool na = 1.5f * fabsf(xa) > bmax, nb = 1.5f * fabsf(xb) > bmax;
+  const double na_e = na ? ea : 0.0f, nb_e = nb ? eb : 0.0f;
+  st.near_sse = __builtin_fma(na_e, na_e, st.near_sse);
+  st.near_sse = __builtin_fma(nb_e, nb_e, st.near_sse);
+  st.near += (uint32_t)na + (uint32_t)nb;
 }
 
 __device__ __forceinline__ void chosen_stats(const float (&x)[16], uint32_t w0, uint32_t w1,
                                              float d, float bmax, LaneStats& st) {
-  const double thr = 2.0 * (double)bmax;   // 3|x| > 2 bmax, exact in binary64
-  pair_stats<0>(w0, x[0], x[1], d, thr, st);
-  pair_stats<1>(w0, x[2], x[3], d, thr, st);
-  pair_stats<2>(w0, x[4], x[5], d, thr, st);
-  pair_stats<3>(w0, x[6], x[7], d, thr, st);
-  pair_stats<0>(w1, x[8], x[9], d, thr, st);
-  pair_stats<1>(w1, x[10], x[11], d, thr, st);
-  pair_stats<2>(w1, x[12], x[13], d, thr, st);
-  pair_stats<3>(w1, x[14], x[15], d, thr, st);
+  pair_stats<0>(w0, x[0], x[1], d, bmax, st);
+  pair_stats<1>(w0, x[2], x[3], d, bmax, st);
+  pair_stats<2>(w0, x[4], x[5], d, bmax, st);
+  pair_stats<3>(w0, x[6], x[7], d, bmax, st);
+  pair_stats<0>(w1, x[8], x[9], d, bmax, st);
+  pair_stats<1>(w1, x[10], x[11], d, bmax, st);
+  pair_stats<2>(w1, x[12], x[13], d, bmax, st);
+  pair_stats<3>(w1, x[14], x[15], d, bmax, st);
 }
 
-// Sum of e^2 of one block when the candidate with target max Q (cq = RN(Q*alpha), cap its
-// largest magnitude code) keeps sigma = RN(bmax / cq) in binary32 as its block scale instead
-// of the E4M3 byte: d = RN(sigma * alpha), the rest as on the reference path.  Kept out of
-// line and rolled, re-reading the block from cache.
-__device__ __noinline__ double f32_scale_sse(const uint16_t* __restrict__ xb, float bmax,
-                                             float alpha, float cq, uint32_t cap) {
-  const float sigma = alpha == 0.0f ? 0.0f : bmax / cq;
-  const float d = sigma * alpha;
-  const float r = d == 0.0f ? 0.0f : 1.0f / d;
-  const bool r_finite = r != __builtin_inff();
+// Sum of e^2 of one block when the chosen candidate (cq = RN(Q*alpha), capv its largest FP4
+// value) keeps sigma = RN(bmax / cq) in binary32 as its block scale instead of the E4M3 byte:
+// d = RN(sigma * alpha), v = RN(|x| * RN(1/d)), FP4 rounding by the hardware conversion
+// (round to nearest even, saturating at 6), value capped at capv, xhat = RN(val * d),
+// e = |x| - xhat (the sign of x does not change e^2).
+// Blocks whose 1/d overflows (alpha far below 2^-118) divide per element instead, out of line.
+__device__ __noinline__ double f32_scale_sse_div(const uint16_t* __restrict__ xb, float d,
+                                                 float capv) {
   double acc = 0.0;
 #pragma unroll 1
   for (int i = 0; i < 16; ++i) {
     const float x = fabsf(__uint_as_float((uint32_t)xb[i] << 16));
-    const float v = r_finite ? x * r : x / d;
-    const uint32_t m = min(e2m1_code_of(v), cap);
-    const double e = (double)(x - e2m1_value_of(m) * d);
+    const float val = fminf(e2m1_value_of(e2m1_code_of(x / d)), capv);
+    const double e = (double)(x - val * d);
     acc = __builtin_fma(e, e, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ double f32_scale_sse(const float (&x)[16],
+                                                const uint16_t* __restrict__ xb, float bmax,
+                                                float alpha, float cq, float capv) {
+  const float sigma = alpha == 0.0f ? 0.0f : bmax / cq;
+  const float d = sigma * alpha;
+  const float r = d == 0.0f ? 0.0f : 1.0f / d;
+  if (r == __builtin_inff()) return f32_scale_sse_div(xb, d, capv);
+  double acc = 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; k += 2) {
+    const float xa = fabsf(x[k]), xc = fabsf(x[k + 1]);
+    const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, xa * r, xc * r, 1.0f, 0);
+    const f32x2 val = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const double ea = (double)(xa - fminf(val.x, capv) * d);
+    const double ec = (double)(xc - fminf(val.y, capv) * d);
+    acc = __builtin_fma(ea, ea, acc);
+    acc = __builtin_fma(ec, ec, acc);
   }
   return acc;
 }
@@ -489,7 +523,7 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     const uint4* __restrict__ in, int64_t nblk, const float* __restrict__ amax,
     uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
     float* __restrict__ alpha_out, uint8_t* __restrict__ qstar, uint32_t* __restrict__ count4,
-    double* __restrict__ stats) {
+    double* __restrict__ stats, uint32_t* __restrict__ stats_ctr, double* __restrict__ stats_slots) {
   __shared__ BlockTables tb;
   const int64_t t = blockIdx.y;
   const uint32_t abits = __float_as_uint(amax[t]) & 0x7FFFFFFFu;
@@ -572,8 +606,9 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
         n_four += four ? 1u : 0u;
         if (want_stats) {
           chosen_stats(x, w0, w1, dq, bm, st);
-          st.f32_sse += f32_scale_sse(reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm,
-                                      alpha, four ? 4.0f * alpha : 6.0f * alpha, four ? 6u : 7u);
+          st.f32_sse += f32_scale_sse(x, reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm,
+                                      alpha, four ? 4.0f * alpha : 6.0f * alpha,
+                                      four ? 4.0f : 6.0f);
         }
       }
     }
@@ -608,6 +643,11 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
         wmx[w] = mx;
       }
       __syncthreads();
+      // This workgroup's partial sums go to its own slot (no two workgroups write one
+      // address).  Each exchange returns once it is performed at device scope, and the
+      // counter increment takes its operand from all six results, so it is issued after them:
+      // the workgroup that brings the counter to G - 1 arrivals finds every slot written.
+      __shared__ int last_sh;
       if (threadIdx.x == 0) {
         double a[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
         float m = 0.0f;
@@ -615,16 +655,56 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
           for (int k = 0; k < 5; ++k) a[k] += wst[w][k];
           m = fmaxf(m, wmx[w]);
         }
-        double* o = stats + t * NVFP4_NSTATS;
-        if (a[0] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_SSE, a[0]);
-        if (a[1] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_SAE, a[1]);
-        if (a[2] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_SSE_NEAR, a[2]);
-        if (a[3] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_SSE_F32SCALE, a[3]);
-        if (a[4] != 0.0) unsafeAtomicAdd(o + NVFP4_STAT_NEAR_COUNT, a[4]);
-        // non-negative binary64 values order like their bit patterns
-        if (m != 0.0f)
-          atomicMax(reinterpret_cast<unsigned long long*>(o + NVFP4_STAT_MAXERR),
-                    (unsigned long long)__double_as_longlong((double)m));
+        u64* slot = reinterpret_cast<u64*>(stats_slots + ((int64_t)t * gridDim.x + blockIdx.x) * kDiagSlot);
+        const u64 r0 = __hip_atomic_exchange(slot + 0, (u64)__double_as_longlong(a[0]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u64 r1 = __hip_atomic_exchange(slot + 1, (u64)__double_as_longlong(a[1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u64 r2 = __hip_atomic_exchange(slot + 2, (u64)__double_as_longlong(a[2]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u64 r3 = __hip_atomic_exchange(slot + 3, (u64)__double_as_longlong(a[3]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u64 r4 = __hip_atomic_exchange(slot + 4, (u64)__double_as_longlong(a[4]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const u64 r5 = __hip_atomic_exchange(slot + 5, (u64)__double_as_longlong((double)m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t one;
+        asm volatile("v_mov_b32 %0, 1" : "=v"(one) : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(r4), "v"(r5));
+        last_sh = __hip_atomic_fetch_add(stats_ctr + t * kDiagCtrWords, one, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+      }
+      __syncthreads();
+      if (last_sh) {      // the last workgroup of the tensor: sum the slots in a fixed order
+        const u64* sl = reinterpret_cast<const u64*>(stats_slots + (int64_t)t * gridDim.x * kDiagSlot);
+        double a[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+        double m = 0.0;
+        for (uint32_t g = threadIdx.x; g < gridDim.x; g += kThreads) {
+          for (int k = 0; k < 5; ++k)
+            a[k] += __longlong_as_double((long long)__hip_atomic_load(sl + g * kDiagSlot + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          m = fmax(m, __longlong_as_double((long long)__hip_atomic_load(sl + g * kDiagSlot + 5, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+        }
+        for (int k = 0; k < 5; ++k) a[k] = wave_sum_f64(a[k]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+        __syncthreads();                             // wst / wmx are reused below
+        if ((threadIdx.x & 63) == 0) {
+          const int w = threadIdx.x >> 6;
+          for (int k = 0; k < 5; ++k) wst[w][k] = a[k];
+          wmx[w] = (float)m;                         // m is a binary32 value
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          double tot[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+          float mt = 0.0f;
+          for (int w = 0; w < kThreads / 64; ++w) {
+            for (int k = 0; k < 5; ++k) tot[k] += wst[w][k];
+            mt = fmaxf(mt, wmx[w]);
+          }
+          // added to what earlier launches over this tensor left (0 before the first)
+          double* o = stats + t * NVFP4_NSTATS;
+          o[NVFP4_STAT_SSE] += tot[0];
+          o[NVFP4_STAT_SAE] += tot[1];
+          o[NVFP4_STAT_SSE_NEAR] += tot[2];
+          o[NVFP4_STAT_SSE_F32SCALE] += tot[3];
+          o[NVFP4_STAT_NEAR_COUNT] += tot[4];
+          o[NVFP4_STAT_MAXERR] = fmax(o[NVFP4_STAT_MAXERR], (double)mt);
+          // the counter is ready for the next launch over this tensor
+          __hip_atomic_store(stats_ctr + t * kDiagCtrWords, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
     }
   }
@@ -941,16 +1021,17 @@ nvfp4_status check_common(const uint16_t* in, const Shape& s, int block, int mod
 }
 
 hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStream_t stream,
-                       uint32_t* acc2 = nullptr, uint32_t* acc3 = nullptr, int64_t n3 = 0) {
+                       uint32_t* acc2 = nullptr, uint32_t* acc3 = nullptr, int64_t n3 = 0,
+                       uint32_t* acc4 = nullptr, int64_t n4 = 0) {
   const int64_t chunks = s.n / 8;
   const int64_t share = std::max<int64_t>(1, kAmaxWGs / s.E);   // workgroups per tensor
   const int64_t want8 = (chunks + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
   const int64_t want1 = (chunks + kAmaxThreads - 1) / kAmaxThreads;
   const bool wide = want8 >= share;
   const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(wide ? want8 : want1, share));
-  const int64_t nclear = std::max<int64_t>(s.E, acc3 ? n3 : 0);
+  const int64_t nclear = std::max({s.E, acc3 ? n3 : 0, acc4 ? n4 : 0});
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((nclear + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, stream, acc, acc2, s.E, acc3, n3);
+                     0, stream, acc, acc2, s.E, acc3, n3, acc4, n4);
   if (wide)
     hipLaunchKernelGGL(amax_kernel<8>, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
                        0, stream, reinterpret_cast<const uint4*>(in), chunks, acc);
@@ -965,7 +1046,10 @@ constexpr int64_t kMaxLaunchBlocks = (INT64_C(1) << 27) - 1;   // 32-bit byte of
 template <int MODE, int RULE, bool FQ, bool DIAG>
 void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, uint8_t* codes,
                        uint8_t* scales, uint16_t* out, float* alpha_out, uint8_t* qstar,
-                       uint32_t* count4, double* stats, hipStream_t stream) {
+                       uint32_t* count4, double* stats, uint32_t* stats_ws, hipStream_t stream) {
+  // statistics workspace: E counter lines, then the slots (reused by consecutive launches)
+  double* const slots = stats_ws ? reinterpret_cast<double*>(stats_ws + s.E * kDiagCtrWords)
+                                 : nullptr;
   auto launch = [&](int64_t E, int64_t nblk, int64_t first_tensor, int64_t first_block) {
     const int64_t one_per_lane = (nblk + kThreads - 1) / kThreads;
     int64_t per_tensor = one_per_lane;
@@ -984,7 +1068,9 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
                        reinterpret_cast<uint4*>(out ? out + b0 * 16 : nullptr),
                        alpha_out ? alpha_out + first_tensor : nullptr, qstar ? qstar + b0 : nullptr,
                        count4 ? count4 + first_tensor : nullptr,
-                       stats ? stats + first_tensor * NVFP4_NSTATS : nullptr);
+                       stats ? stats + first_tensor * NVFP4_NSTATS : nullptr,
+                       stats ? stats_ws + first_tensor * kDiagCtrWords : nullptr,
+                       stats ? slots : nullptr);
   };
   if (s.nblk <= kMaxLaunchBlocks) {
     launch(s.E, s.nblk, 0, 0);
@@ -998,19 +1084,20 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
 template <bool FQ, bool DIAG>
 void launch_quantize(int mode, int rule, const uint16_t* in, const Shape& s, const float* amax,
                      uint8_t* codes, uint8_t* scales, uint16_t* out, float* alpha_out,
-                     uint8_t* qstar, uint32_t* count4, double* stats, hipStream_t stream) {
+                     uint8_t* qstar, uint32_t* count4, double* stats, uint32_t* stats_ws,
+                     hipStream_t stream) {
   if (mode == NVFP4_RTN6) {
     launch_quantize_t<NVFP4_RTN6, NVFP4_RULE_MSE, FQ, DIAG>(in, s, amax, codes, scales, out,
-                                                            alpha_out, qstar, count4, stats, stream);
+                                                            alpha_out, qstar, count4, stats, stats_ws, stream);
   } else if (rule == NVFP4_RULE_MSE) {
     launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MSE, FQ, DIAG>(
-        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stream);
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stats_ws, stream);
   } else if (rule == NVFP4_RULE_MAE) {
     launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAE, FQ, DIAG>(
-        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stream);
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stats_ws, stream);
   } else {
     launch_quantize_t<NVFP4_FOUR_OVER_SIX, NVFP4_RULE_MAXERR, FQ, DIAG>(
-        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stream);
+        in, s, amax, codes, scales, out, alpha_out, qstar, count4, stats, stats_ws, stream);
   }
 }
 
@@ -1063,7 +1150,8 @@ nvfp4_status validate_main(const uint16_t* in, int64_t E, int64_t rows, int64_t 
 nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int block, int mode,
                  int rule, const float* amax_in, uint8_t* codes, uint8_t* scales, uint16_t* out,
                  float* alpha, bool fq, hipStream_t stream, uint8_t* qstar = nullptr,
-                 uint32_t* count4 = nullptr, double* stats = nullptr) {
+                 uint32_t* count4 = nullptr, double* stats = nullptr,
+                 uint32_t* stats_ws = nullptr) {
   Shape s;
   nvfp4_status st = validate_main(in, E, rows, cols, block, mode, rule, amax_in, codes, scales,
                                   out, alpha, fq, &s);
@@ -1087,6 +1175,14 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
           overlap(stats, sb, scales, s.E * s.nblk) || overlap(stats, sb, alpha, s.E * 4) ||
           overlap(stats, sb, qstar, qb) || overlap(stats, sb, count4, s.E * 4))
         return NVFP4_ERR_ALIAS;
+      if (!stats_ws) return NVFP4_ERR_NULL;
+      if (!aligned(stats_ws, 128)) return NVFP4_ERR_ALIGN;
+      const int64_t wb = NVFP4_DIAG_WS_WORDS(s.E) * 4;
+      if (overlap(stats_ws, wb, in, in_bytes2) || overlap(stats_ws, wb, codes, s.E * s.n / 2) ||
+          overlap(stats_ws, wb, scales, s.E * s.nblk) || overlap(stats_ws, wb, alpha, s.E * 4) ||
+          overlap(stats_ws, wb, qstar, qb) || overlap(stats_ws, wb, count4, s.E * 4) ||
+          overlap(stats_ws, wb, stats, sb))
+        return NVFP4_ERR_ALIAS;
     }
   }
 
@@ -1094,8 +1190,8 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
   const float* amax = amax_in;
   if (!amax) {
     if (launch_amax(in, s, reinterpret_cast<uint32_t*>(alpha), stream, count4,
-                    reinterpret_cast<uint32_t*>(stats), stats ? s.E * NVFP4_NSTATS * 2 : 0) !=
-        hipSuccess)
+                    reinterpret_cast<uint32_t*>(stats), stats ? s.E * NVFP4_NSTATS * 2 : 0,
+                    stats ? stats_ws : nullptr, stats ? s.E * kDiagCtrWords : 0) != hipSuccess)
       return NVFP4_ERR_HIP;
     amax = alpha;
   }
@@ -1104,13 +1200,13 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
   float* alpha_in_kernel = amax == alpha ? nullptr : alpha;
   if (fq)
     launch_quantize<true, false>(mode, rule, in, s, amax, nullptr, nullptr, out, alpha_in_kernel,
-                                 nullptr, nullptr, nullptr, stream);
+                                 nullptr, nullptr, nullptr, nullptr, stream);
   else if (diag)
     launch_quantize<false, true>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
-                                 qstar, count4, stats, stream);
+                                 qstar, count4, stats, stats ? stats_ws : nullptr, stream);
   else
     launch_quantize<false, false>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
-                                  nullptr, nullptr, nullptr, stream);
+                                  nullptr, nullptr, nullptr, nullptr, stream);
   if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
   if (!alpha_in_kernel &&
       launch_alpha(reinterpret_cast<const uint32_t*>(amax), alpha, s, mode, stream) != hipSuccess)
@@ -1154,7 +1250,8 @@ void fused_launch(int64_t G, const uint16_t* in, const Shape& s, uint32_t* ws, u
                   uint8_t* scales, uint16_t* out, float* alpha, hipStream_t stream) {
   const int64_t words = s.E * kFusedWsWords;
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((words + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, stream, ws, nullptr, words, nullptr, (int64_t)0);
+                     dim3(kThreads), 0, stream, ws, nullptr, words, nullptr, (int64_t)0, nullptr,
+                     (int64_t)0);
   hipLaunchKernelGGL((fused_kernel<MODE, RULE, FQ, KR, KL>), dim3((unsigned)G, (unsigned)s.E),
                      dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(in), s.nblk, ws,
                      reinterpret_cast<uint2*>(codes), scales, reinterpret_cast<uint4*>(out), alpha,
@@ -1332,10 +1429,11 @@ NVFP4_EXPORT nvfp4_status nvfp4_quantize_diag(const uint16_t* in, int64_t E, int
                                               nvfp4_rule rule, uint8_t* out_codes,
                                               uint8_t* out_scales, float* out_alpha,
                                               uint8_t* out_qstar, uint32_t* out_count4,
-                                              double* out_stats, hipStream_t stream) {
+                                              double* out_stats, uint32_t* stats_workspace,
+                                              hipStream_t stream) {
   if (!out_qstar || !out_count4) return NVFP4_ERR_NULL;
   return run(in, E, rows, cols, block, mode, rule, nullptr, out_codes, out_scales, nullptr,
-             out_alpha, false, stream, out_qstar, out_count4, out_stats);
+             out_alpha, false, stream, out_qstar, out_count4, out_stats, stats_workspace);
 }
 
 NVFP4_EXPORT nvfp4_status nvfp4_quantize_from_amax(const uint16_t* in, int64_t E, int64_t rows,

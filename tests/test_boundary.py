@@ -50,7 +50,7 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.nvfp4_abi_version() == 3
+    assert L.nvfp4_abi_version() == 4
     for st in range(8):
         assert L.nvfp4_status_str(st)
     assert L.nvfp4_status_str(99) == b"unknown status"
@@ -127,14 +127,22 @@ def test_dequantize_validation(L):
 
 def test_diag_validation(L):
     f = L.nvfp4_quantize_diag
-    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, None, D + 64, None, None) == ENULL
-    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, None, None, None) == ENULL
-    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 66, None, None) == EALIGN
-    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C, D + 64, None, None) == EALIAS       # qstar over scales
-    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, A + 8, None, None) == EALIAS  # count4 in input
-    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 132, None) == EALIGN   # stats
-    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 64, None) == EALIAS    # over count4
-    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, A + 64, None) == EALIAS    # in input
+    W = 0x2100000
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, None, D + 64, None, None, None) == ENULL
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, None, None, None, None) == ENULL
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 66, None, None, None) == EALIGN
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C, D + 64, None, None, None) == EALIAS    # qstar over scales
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, A + 8, None, None, None) == EALIAS  # count4 in input
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 132, W, None) == EALIGN  # stats
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 64, W, None) == EALIAS   # over count4
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, A + 64, W, None) == EALIAS   # in input
+    # the statistics workspace: required with stats, 128-byte aligned, apart from the rest
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 128, None, None) == ENULL
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 128, W + 64, None) == EALIGN
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 128, A + 128, None) == EALIAS
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 128, D + 128, None) == EALIAS
+    assert f(A, 1, 4, 32, 16, 1, 0, B, C, D, C + 1024, D + 64, W, C + 896, None) == EALIAS  # over qstar
+    assert f(A, 1, 4, 30, 16, 1, 0, B, C, D, C + 1024, D + 64, D + 128, W, None) == ESHAPE
 
 
 def test_fused_validation(L):

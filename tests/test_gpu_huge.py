@@ -4,8 +4,9 @@ Block indices inside a kernel are 32-bit, so the host splits the block pass of a
 2^27 blocks or more into launches over consecutive block ranges (offset pointers, one tensor
 per launch).  This runs the dynamic packed, fake-quant and diagnostics calls on a
 131080 x 16384 bf16 tensor (2^27 + 8192 blocks, 4.3 GB) and compares the whole packed output,
-alpha, the count of blocks scaled to 4, and sampled fake-quant and dequantized blocks around
-the launch boundary with the oracle (dequantize splits its launches the same way)."""
+alpha, the count of blocks scaled to 4, the error statistics (summed over both launches), and
+sampled fake-quant and dequantized blocks around the launch boundary with the oracle
+(dequantize splits its launches the same way)."""
 from __future__ import annotations
 
 import os
@@ -16,6 +17,7 @@ import pytest
 import torch
 
 from nvfp4_block_scaled_amax_amd import workloads as W
+from test_gpu_parity import check_stats
 
 pytestmark = pytest.mark.gpu
 
@@ -48,11 +50,11 @@ def test_tensor_over_2pow27_blocks(nv, orc):
 
     say("[huge] packed, four_over_six/mse")
     c, s, a = nv.quantize(xg, "four_over_six", "mse")
-    cq, sq, aq, q, n4, _ = nv.quantize_diag(xg, "four_over_six", "mse", stats=False)
+    cq, sq, aq, q, n4, stg = nv.quantize_diag(xg, "four_over_six", "mse")
     torch.cuda.synchronize()
     assert torch.equal(cq, c) and torch.equal(sq, s) and torch.equal(aq, a)
     codes, scales = c.cpu().numpy(), s.cpu().numpy()
-    qstar_gpu, n4_gpu = q.cpu().numpy(), int(n4.cpu()[0])
+    qstar_gpu, n4_gpu, stats_gpu = q.cpu().numpy(), int(n4.cpu()[0]), stg.cpu().numpy()
     del cq, sq, q
 
     say("[huge] dequantize, sampled around the launch boundary")
@@ -77,6 +79,10 @@ def test_tensor_over_2pow27_blocks(nv, orc):
     assert np.array_equal(qstar_gpu, ref["qstar"])
     assert n4_gpu == int((ref["qstar"] == 4).sum()) > 0
     del codes, scales, ref, qstar_gpu
+
+    say("[huge] oracle statistics, whole tensor")
+    check_stats(stats_gpu, orc.quantize_stats(x, "four_over_six", "mse", nthreads=NTHREADS),
+                x.size, "huge")
 
     say("[huge] fake-quant, rtn6, sampled around the launch boundary")
     y, a2 = nv.fakequant(xg, "rtn6", "mse")

@@ -444,6 +444,25 @@ def test_diag_poison_and_edges(nv, orc):
     assert np.isnan(st.cpu().numpy()).sum() == 0
 
 
+@pytest.mark.parametrize("shape", [(1024, 8208), (4, 300, 640), (1100, 2, 32)],
+                         ids=["one-tensor", "batched", "more-tensors-than-slots"])
+def test_diag_stats_repeatable_with_any_workspace(nv, orc, shape):
+    """The statistics are summed in an order fixed by the shape: repeated calls give the same
+    bits, whatever the workspace held before (here all ones, then random words)."""
+    x = W.bits(W.weight(shape, seed=41))
+    E = shape[0] if len(shape) == 3 else 1
+    xg = to_gpu(x)
+    ws = torch.full((nv.diag_ws_words(E),), -1, dtype=torch.int32, device="cuda")
+    first = nv.quantize_diag(xg, "four_over_six", "mse", workspace=ws)[5].cpu().numpy()
+    ws.copy_(torch.randint(-2**31, 2**31 - 1, ws.shape, dtype=torch.int32))
+    again = nv.quantize_diag(xg, "four_over_six", "mse", workspace=ws)[5].cpu().numpy()
+    third = nv.quantize_diag(xg, "four_over_six", "mse")[5].cpu().numpy()
+    assert np.array_equal(first.view(np.uint64), again.view(np.uint64))
+    assert np.array_equal(first.view(np.uint64), third.view(np.uint64))
+    check_stats(first, orc.quantize_stats(x, "four_over_six", "mse", nthreads=NTHREADS),
+                x.size // E, str(shape))
+
+
 DIAG_FULL = [(w.name, mode, rule) for w in W.WORKLOADS.values()
              for (mode, rule, _) in w.runs[:1]]
 
