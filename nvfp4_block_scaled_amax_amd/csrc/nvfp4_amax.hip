@@ -187,6 +187,7 @@ constexpr int64_t kLongLaunchBlocks = INT64_C(1) << 23;
 constexpr int64_t kShortLaunchWGs = 1024;
 constexpr int64_t kLaneBlocksLong = 4;
 constexpr int64_t kDiagLaunchWGs = 1024;
+constexpr uint32_t kPacedSteps = 8;      // grid-stride steps per lane from which waves pace themselves
 constexpr int kDiagCtrWords = 32;        // statistics workspace: one 128-byte counter line per tensor
 constexpr int kDiagSlot = NVFP4_NSTATS;  // and six binary64 partials per workgroup
 static_assert(NVFP4_DIAG_WS_WORDS(1) == kDiagCtrWords + 2 * kDiagSlot * kDiagLaunchWGs &&
@@ -574,7 +575,23 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     nx0 = *reinterpret_cast<const uint4*>(inT + (u << 5));
     nx1 = *reinterpret_cast<const uint4*>(inT + (u << 5) + 16);
   }
-  for (; u < n; u += stride) {
+  // Waves that start together on a SIMD do not progress together: issue goes to the oldest
+  // ready wave, so in a grid that strides over many blocks per lane some waves finish far
+  // ahead of others and the launch ends with few waves in flight.  With 8 or more steps per
+  // lane, each wave lowers its issue priority at a quarter, half and three quarters of its
+  // steps, so the waves that are behind are issued first.  (Fewer steps: the hardware's
+  // dispatch of many workgroups balances the load instead.)
+  const uint32_t u_first = (uint32_t)__builtin_amdgcn_readfirstlane(u);
+  const uint32_t steps = u_first < n ? (n - u_first + stride - 1) / stride : 0;  // wave-uniform
+  const bool pace = steps >= kPacedSteps;
+  const uint32_t q1 = steps / 4, q2 = steps / 2, q3 = (3 * steps) / 4;
+  if (pace) __builtin_amdgcn_s_setprio(3);
+  for (uint32_t step = 0; u < n; u += stride, ++step) {
+    if (pace) {
+      if (step == q1) __builtin_amdgcn_s_setprio(2);
+      if (step == q2) __builtin_amdgcn_s_setprio(1);
+      if (step == q3) __builtin_amdgcn_s_setprio(0);
+    }
     const uint4 c0 = nx0, c1 = nx1;
     const uint32_t un = min(u + stride, n - 1);   // always in bounds: reloads the last block
     nx0 = *reinterpret_cast<const uint4*>(inT + (un << 5));
@@ -920,8 +937,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   build_tables<MODE>(tb, alpha, n6, n4);
   __syncthreads();
   const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
+  // Phase 2 is bound by the VALU and every workgroup starts it at once: the waves pace
+  // themselves as in quantize_kernel (issue priority 3, 2, 1, 0 by quarters of the held blocks).
+  constexpr int K = KR + KL;
+  constexpr bool pace = K >= (int)kPacedSteps;
+  if (pace) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
   for (int k = 0; k < KR; ++k) {
+    if (pace && k == K / 4) __builtin_amdgcn_s_setprio(2);
+    if (pace && k == K / 2) __builtin_amdgcn_s_setprio(1);
+    if (pace && k == (3 * K) / 4) __builtin_amdgcn_s_setprio(0);
     const uint32_t u = ((uint32_t)k * G + g) * kThreads + tid;
     if (u < n)
       fused_emit<MODE, RULE, FQ>(r0[k], r1[k], u, inT, codesT, scalesT, outT, tb, n6, n4,
@@ -929,6 +954,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 #pragma unroll
   for (int k = 0; k < KL; ++k) {
+    if (pace && KR + k == K / 4) __builtin_amdgcn_s_setprio(2);
+    if (pace && KR + k == K / 2) __builtin_amdgcn_s_setprio(1);
+    if (pace && KR + k == (3 * K) / 4) __builtin_amdgcn_s_setprio(0);
     const uint32_t u = ((uint32_t)(KR + k) * G + g) * kThreads + tid;
     if (u < n)
       fused_emit<MODE, RULE, FQ>(held[k][0][tid], held[k][1][tid], u, inT, codesT, scalesT,
