@@ -337,7 +337,7 @@ def cpu_baseline(x_cpu, wl, args, step_bpe):
         desc = "first %d of %d rows (%d elements)" % (rows, x.shape[0], sample.size)
     oracle.build()
     reps, times = 0, []
-    while reps < 20 and (reps < 3 or sum(times) < 10.0):     # about 10 s of wall clock
+    while reps < 60 and (reps < 3 or sum(times) < 12.0):     # about 12 s of wall clock
         t0 = time.perf_counter()
         oracle.quantize(sample, args.mode, args.rule, nthreads=cores, want_y=False)
         times.append(time.perf_counter() - t0)
