@@ -52,9 +52,32 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def source_digest(path: str = KERNEL_SRC) -> str:
+    """First 16 hex digits of the SHA-256 of the kernel source's code: comments removed and
+    runs of white space folded to one space, so that an edit to comments or layout alone
+    keeps the committed counters, and any change to device or host code drops them."""
+    text = open(path, encoding="utf-8").read()
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                                    # string or character literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    code = " ".join("".join(out).split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def read_counters(workload, mode, rule):

@@ -211,7 +211,7 @@ int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols, nvfp4_mode mo
                             nvfp4_rule rule, int fakequant);
 
 /* Test hook (process-wide, the library's only setting): how many times a workgroup of a
- * single-read launch polls for the other workgroups (about 0.2 us each) before it computes
+ * single-read launch polls for the other workgroups (about 1 us each) before it computes
  * the tensor amax itself.  0 = never wait; a negative value restores the default (2^20);
  * larger values are capped at 2^26, so that a wait always ends. */
 void nvfp4_fused_set_wait_limit(int64_t polls);

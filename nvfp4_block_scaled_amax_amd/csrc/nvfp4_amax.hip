@@ -183,6 +183,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //     from 2^23 blocks on, 4 blocks per lane beat 1024 or 768 workgroups by 4-12 % (MoE 10 %).
 //   - The diagnostics variant ends with one or two same-address atomics per workgroup (the
 //     count of blocks scaled to 4, the statistics counter): 1024 workgroups in all.
+//   With paced waves (see the block-pass loop) the choices were measured again: 768, 1536 or
+//   2048 workgroups, 8 or 16 blocks per lane, 2048 or 4096 workgroups for long launches, and
+//   1024-4096 workgroups for rtn6 and fake-quant were all slower or equal.
 constexpr int64_t kLongLaunchBlocks = INT64_C(1) << 23;
 constexpr int64_t kShortLaunchWGs = 1024;
 constexpr int64_t kLaneBlocksLong = 4;
@@ -382,8 +385,9 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
 // of NVFP4_STAT_*): sum e^2, sum |e|, max |e|, sum e^2 over the elements above 2/3 of their
 // block max, sum e^2 if the chosen candidate kept its binary32 block scale, and the count of
 // elements above 2/3 of their block max.  e = x - xhat is exact in binary32, so e^2 is exact
-// in binary64; the sums are binary64 (lane, then wavefront, then workgroup, then one atomic
-// per workgroup), so only their rounding depends on the order.
+// in binary64; the sums are binary64 (lane, then wavefront, then workgroup, then the
+// workgroups' partials summed by the last workgroup), so only their rounding depends on the
+// order, and the launch shape fixes that order.
 struct LaneStats {
   double sse, sae, near_sse, f32_sse;
   float mx;
@@ -663,7 +667,7 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
       // This workgroup's partial sums go to its own slot (no two workgroups write one
       // address).  Each exchange returns once it is performed at device scope, and the
       // counter increment takes its operand from all six results, so it is issued after them:
-      // the workgroup that brings the counter to G - 1 arrivals finds every slot written.
+      // the workgroup whose increment finds G - 1 earlier arrivals finds every slot written.
       __shared__ int last_sh;
       if (threadIdx.x == 0) {
         double a[5] = {0.0, 0.0, 0.0, 0.0, 0.0};

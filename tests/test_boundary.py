@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 import torch
@@ -193,3 +194,25 @@ def test_build_rejects_kernels_that_spill():
         "k.hip:9:1: remark:     ScratchSize [bytes/lane]: 24 [-Rpass-analysis=kernel-resource-usage]"])
     assert build.scratch_users(report) == [("b_kernel", 24)]
     assert build.scratch_users(report.replace(": 24 ", ": 0 ")) == []
+
+
+def test_counter_digest_ignores_comments_only(tmp_path):
+    """The committed HBM-traffic figure is tied to the kernel source's code: comments and
+    layout do not change the digest, code and string literals do."""
+    sys.path.insert(0, ROOT)
+    import bench
+    base = 'int a = 1; // note\n/* block */ const char* s = "x // y"; char q = \'"\';\n'
+    variants = {
+        "comment": ('int a = 1;   // another note\n/* other */ const char* s = "x // y"; '
+                    'char q = \'"\';\n', True),
+        "code": ('int a = 2; // note\n/* block */ const char* s = "x // y"; char q = \'"\';\n',
+                 False),
+        "literal": ('int a = 1; // note\n/* block */ const char* s = "x // z"; char q = \'"\';\n',
+                    False),
+    }
+    p = tmp_path / "k.hip"
+    p.write_text(base)
+    d0 = bench.source_digest(str(p))
+    for name, (text, same) in variants.items():
+        p.write_text(text)
+        assert (bench.source_digest(str(p)) == d0) == same, name
