@@ -90,6 +90,10 @@ def test_quantize_rejects_bad_arguments(L):
     assert q(L, codes=A + 16) == EALIAS            # codes overlap the input
     assert q(L, alpha=A + 64) == EALIAS            # the amax accumulator overlaps the input
     assert q(L, scales=B + 8) == EALIAS            # scales overlap codes
+    qb = L.nvfp4_quantize_batched
+    assert qb(A, 65536, 1, 16, 16, 1, 0, B, C, D, None) == ESHAPE   # grid y holds 65535 tensors
+    assert qb(A, 0, 1, 16, 16, 1, 0, B, C, D, None) == ESHAPE
+    assert qb(A, 65535, 1, 16, 16, 1, 0, B, C, A, None) == EALIAS   # shape accepted; alpha in input
 
 
 def test_fakequant_rejects_bad_arguments_and_partial_overlap(L):
