@@ -21,7 +21,8 @@ import torch
 
 __all__ = ["quantize", "fakequant", "amax", "quantize_from_amax", "fakequant_from_amax",
            "dequantize", "quantize_diag", "quantize_fused", "fakequant_fused",
-           "fused_blocks_per_lane", "set_fused_wait_limit", "lib", "NVFP4Error", "MODES", "RULES", "LIB_PATH"]
+           "fused_blocks_per_lane", "set_fused_wait_limit", "diag_ws_words", "lib",
+           "NVFP4Error", "MODES", "RULES", "STATS", "FUSED_WS_WORDS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_amax.so")
 MODES = {"rtn6": 0, "four_over_six": 1}
@@ -79,9 +80,10 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_fused_single_read.restype = i32
         L.nvfp4_fused_set_wait_limit.argtypes = [i64]
         L.nvfp4_fused_set_wait_limit.restype = None
-        for name in ("nvfp4_quantize_fused", "nvfp4_fakequant_fused", "nvfp4_quantize_diag", "nvfp4_dequantize", "nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
+        for name in ("nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
                      "nvfp4_fakequant_batched", "nvfp4_quantize_from_amax",
-                     "nvfp4_fakequant_from_amax"):
+                     "nvfp4_fakequant_from_amax", "nvfp4_dequantize", "nvfp4_quantize_diag",
+                     "nvfp4_quantize_fused", "nvfp4_fakequant_fused"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

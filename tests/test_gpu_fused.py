@@ -69,6 +69,22 @@ def test_fused_small_whole(nv, orc, name, shape, mode, rule, fq):
     assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq, name)
 
 
+def test_fused_random_shapes(nv, orc):
+    """Random shapes with ragged last workgroups, batched or not, every mode and rule, both
+    outputs, values spread over 2^-8 to 2^8 in scale."""
+    rng = np.random.default_rng(91)
+    for k in range(24):
+        rows = int(rng.integers(1, 40))
+        cols = int(rng.integers(1, 200)) * 16
+        E = int(rng.integers(2, 6)) if k % 3 == 0 else None
+        shape = (E, rows, cols) if E else (rows, cols)
+        x = W.bits(W.normal(shape, seed=2000 + k, sigma=float(np.exp(rng.uniform(-8, 8)))))
+        mode, rule = RUNS[k % 4]
+        fq = bool((k // 4) % 2)
+        assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq,
+                              "random%d %s" % (k, shape))
+
+
 # Shapes that select each tier on a 256-CU MI355X (the test checks the tier it gets).
 TIERS = [(1, (256, 256)), (4, (1024, 8208)), (12, (4096, 8448)), (28, (4096, 14336))]
 

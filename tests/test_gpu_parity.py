@@ -342,6 +342,26 @@ def test_full_size_workloads_whole(nv, orc, name, mode, rule, fq):
 
 
 # ----------------------------------------------------------------------------- dequantize
+def test_dequantize_random_shapes_and_bytes(nv, orc):
+    """Random shapes (ragged last workgroups, batched or not) with arbitrary code bytes, scale
+    bytes (NaN and negative scales included) and alphas, against the oracle's dequantization."""
+    rng = np.random.default_rng(93)
+    for k in range(16):
+        rows = int(rng.integers(1, 40))
+        cols = int(rng.integers(1, 200)) * 16
+        E = int(rng.integers(2, 5)) if k % 2 else 1
+        lead = (E,) if k % 2 else ()
+        codes = rng.integers(0, 256, size=lead + (rows, cols // 2), dtype=np.uint8)
+        scales = rng.integers(0, 256, size=lead + (rows, cols // 16), dtype=np.uint8)
+        alpha = np.exp(rng.uniform(-20, 5, size=E)).astype(np.float32)
+        y = nv.dequantize(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                          torch.from_numpy(alpha).cuda())
+        torch.cuda.synchronize()
+        ref = orc.dequantize(codes.reshape((E, rows, cols // 2)),
+                             scales.reshape((E, rows, cols // 16)), alpha)
+        assert np.array_equal(u16(y).reshape(-1), ref.reshape(-1)), (k, rows, cols, E)
+
+
 @pytest.mark.parametrize("name,shape", SMALL, ids=[s[0] for s in SMALL])
 def test_dequantize_equals_fakequant_and_oracle(nv, orc, name, shape):
     x = W.bits(W.generate(name, shape))
