@@ -216,8 +216,9 @@ def main():
                 fn(i % R)
         return g
 
-    def replay_avg_us(g, count, reps=3):
-        """Median over reps of (events around one replay) / count, in microseconds."""
+    def replay_us(g, count, reps=5):
+        """(events around one replay) / count in microseconds, over reps replays:
+        (median, min, max)."""
         out = []
         for _ in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -226,7 +227,7 @@ def main():
             b.record()
             torch.cuda.synchronize()
             out.append(a.elapsed_time(b) * 1e3 / count)
-        return float(np.median(out))
+        return float(np.median(out)), float(np.min(out)), float(np.max(out))
 
     # ---- timed region: K steps in one graph, replayed once
     K = args.steps
@@ -252,7 +253,7 @@ def main():
             nv.quantize_from_amax(xs[i], amaxs[i], args.mode, args.rule, codes=pk[i][0],
                                   scales=pk[i][1], alpha=alphas[i])
     torch.cuda.synchronize()
-    legs = {}
+    legs, spread = {}, {}
     for name, fn in (("block", block_pass),
                      ("rtn6_block", lambda i: block_pass(i, "rtn6", "mse")),
                      ("block_again", block_pass),          # 4/6 once more: drift check
@@ -261,12 +262,16 @@ def main():
                      ("fused_entry_point", fused_call),
                      ("diagnostics", lambda i: diag_call(i, False)),
                      ("diagnostics_with_stats", lambda i: diag_call(i, True)),
-                     ("dequantize", dequant_call)):
+                     ("dequantize", dequant_call),
+                     ("block_warm", lambda i: block_pass(0))):   # one buffer set: input in cache
         g = capture(fn, B)
-        legs[name] = replay_avg_us(g, B)
+        legs[name], lo, hi = replay_us(g, B)
+        spread[name] = [round(lo, 2), round(hi, 2)]
         del g
-        log("[bench] leg %s: %.2f us per launch" % (name, legs[name]))
-    t_block = min(legs["block"], legs["block_again"])
+        log("[bench] leg %s: %.2f us per launch (min %.2f, max %.2f over replays)"
+            % (name, legs[name], lo, hi))
+    block_leg = "block" if legs["block"] <= legs["block_again"] else "block_again"
+    t_block = legs[block_leg]
     t_rtn6 = legs["rtn6_block"]
     block_gbps = pass_bpe * N / (t_block * 1e-6) / 1e9
 
@@ -290,11 +295,17 @@ def main():
         },
         "passes": {
             "block": {"avg_us": round(t_block, 2), "GBps": round(block_gbps, 1),
-                      "frac_hbm": round(block_gbps / HBM_PEAK_GBPS, 4)},
+                      "frac_hbm": round(block_gbps / HBM_PEAK_GBPS, 4),
+                      "Gelem_per_s": round(N / (t_block * 1e-6) / 1e9, 2),
+                      "replay_min_max_us": spread[block_leg],
+                      "warm_avg_us": round(legs["block_warm"], 2)},
             "rtn6_block": {"avg_us": round(t_rtn6, 2),
-                           "GBps": round(pass_bpe * N / (t_rtn6 * 1e-6) / 1e9, 1)},
+                           "GBps": round(pass_bpe * N / (t_rtn6 * 1e-6) / 1e9, 1),
+                           "replay_min_max_us": spread["rtn6_block"]},
             "amax": {"avg_us": round(legs["amax"], 2),
-                     "GBps": round(AMAX_BPE * N / (legs["amax"] * 1e-6) / 1e9, 1)},
+                     "GBps": round(AMAX_BPE * N / (legs["amax"] * 1e-6) / 1e9, 1),
+                     "replay_min_max_us": spread["amax"]},
+            "step": {"Gelem_per_s": round(N / (ms_step * 1e-3) / 1e9, 2)},
             "dynamic_entry_point": {"avg_us": round(legs["dynamic_entry_point"], 2)},
             "fused_entry_point": {
                 "avg_us": round(legs["fused_entry_point"], 2),
@@ -366,9 +377,32 @@ def cpu_baseline(x_cpu, wl, args, step_bpe):
         times.append(time.perf_counter() - t0)
         reps += 1
     dt = float(np.median(times))
+    # one thread, on the first eighth of the sample (about 1 s per run), median of 3
+    small = sample[: max(1, sample.shape[0] // 8)]
+    t1 = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.quantize(small, args.mode, args.rule, nthreads=1, want_y=False)
+        t1.append(time.perf_counter() - t0)
+    dt1 = float(np.median(t1))
     return {"value": round(step_bpe * sample.size / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "sample": desc + ", median of %d runs" % reps,
-            "seconds_per_run": round(dt, 3)}
+            "seconds_per_run": round(dt, 3), "cpu_model": cpu_model(),
+            "single_thread": {"value": round(step_bpe * small.size / dt1 / 1e9, 4),
+                              "unit": "GB/s", "cores": 1,
+                              "sample": "first %d elements of that sample, median of 3 runs"
+                                        % small.size,
+                              "seconds_per_run": round(dt1, 3)}}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
