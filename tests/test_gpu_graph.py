@@ -54,6 +54,19 @@ def test_graph_replays_match_eager(nv, orc, shape, mode, rule):
     codes3, scales3, alpha3 = torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(alpha)
     y3, alpha_y3 = torch.empty_like(x), torch.empty_like(alpha)
     ws = torch.empty(nv.FUSED_WS_WORDS * E, dtype=torch.int32, device="cuda")
+    dws = torch.empty(nv.diag_ws_words(E), dtype=torch.int32, device="cuda")
+    codes4, scales4, alpha4 = torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(alpha)
+    qstar = torch.empty_like(scales)
+    count4 = torch.empty(E, dtype=torch.int32, device="cuda")
+    stats = torch.empty((E, len(nv.STATS)), dtype=torch.float64, device="cuda")
+
+    def diag():
+        st = nv.lib().nvfp4_quantize_diag(
+            x.data_ptr(), E, shape[-2], shape[-1], 16, nv.MODES[mode], nv.RULES[rule],
+            codes4.data_ptr(), scales4.data_ptr(), alpha4.data_ptr(), qstar.data_ptr(),
+            count4.data_ptr(), stats.data_ptr(), dws.data_ptr(),
+            torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
 
     def work():
         nv.quantize(x, mode, rule, codes=codes, scales=scales, alpha=alpha)
@@ -62,11 +75,12 @@ def test_graph_replays_match_eager(nv, orc, shape, mode, rule):
         nv.quantize_from_amax(x, am, mode, rule, codes=codes2, scales=scales2, alpha=alpha2)
         nv.quantize_fused(x, mode, rule, codes=codes3, scales=scales3, alpha=alpha3, workspace=ws)
         nv.fakequant_fused(x, mode, rule, out=y3, alpha=alpha_y3, workspace=ws)
+        diag()                                    # statistics: counters reset by the call
 
     work()
     torch.cuda.synchronize()
     outs = (codes, scales, alpha, y, alpha_y, am, codes2, scales2, alpha2, codes3, scales3,
-            alpha3, y3, alpha_y3)
+            alpha3, y3, alpha_y3, codes4, scales4, alpha4, qstar, count4, stats)
     ref = [t.clone() for t in outs]
     g = _capture(work)
     for r in range(4):
@@ -84,3 +98,4 @@ def test_graph_replays_match_eager(nv, orc, shape, mode, rule):
     assert np.array_equal(codes.cpu().numpy(), o["codes"])
     assert np.array_equal(W.bits(y.cpu()), o["y"])
     assert torch.equal(codes3, codes) and torch.equal(y3, y) and torch.equal(alpha3, alpha)
+    assert torch.equal(codes4, codes) and torch.equal(scales4, scales)
