@@ -206,7 +206,9 @@ nvfp4_status nvfp4_fakequant_fused(const uint16_t* in, int64_t E, int64_t rows, 
 /* For a fused call of this shape, mode, rule and output form on the current device: the
  * number of blocks each lane holds on chip (1, 4, 12 or 28) if it reads its input once, 0 if
  * it takes the two-pass path, or minus a status code for bad arguments.  On MI355X up to
- * 3,670,016 blocks per tensor launch (E * rows * cols / 16; 117 MB of bf16) read once. */
+ * 3,670,016 blocks per launch (E * rows * cols / 16; 117 MB of bf16) are held at once.  A larger
+ * batch whose single tensors fit (up to 2,621,440 blocks each) is read once too, by teams of
+ * workgroups that take its tensors in turn: the call then returns 20. */
 int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols, nvfp4_mode mode,
                             nvfp4_rule rule, int fakequant);
 

@@ -3,6 +3,7 @@
 The fused entry points must give the dynamic entry points' results bit for bit: codes, scale
 bytes, alpha bits and fake-quant bf16 bits equal to the oracle's.  Covered here: every tier of
 blocks held per lane (1, 4, 12 and 28, confirmed through the shape query), the batched form,
+batches run in teams (20 per lane; the 64-expert MoE batch whole),
 the edge tensors, poisoning, the bounded grid-wide wait forced from the host (every workgroup
 or some of them computing the tensor amax alone), the two-pass route for tensors that do not
 fit on chip and for in-place fake-quant, and a workspace that starts with arbitrary content."""
@@ -148,6 +149,49 @@ def test_fused_bounded_wait_fallback(nv, orc, limit, shape):
                                   "limit%d" % limit)
     finally:
         nv.set_fused_wait_limit(-1)
+
+
+# Batches that no tier holds at once but whose single tensors fit: teams of workgroups take the
+# tensors in turn (20 blocks per lane; odd teams start half a cycle late).
+TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),
+         ((5, 1000, 14336), "four_over_six", "mae", True),
+         ((12, 512, 14336), "rtn6", "mse", False),
+         ((3, 2048, 14336), "four_over_six", "maxerr", False)]
+
+
+@pytest.mark.parametrize("shape,mode,rule,fq", TEAMS, ids=["t%d" % i for i in range(len(TEAMS))])
+def test_fused_teams_whole_batch(nv, orc, shape, mode, rule, fq):
+    tier = nv.fused_blocks_per_lane(shape, mode, rule, fq)
+    say("[fused-teams] %s %s/%s fq=%s: %d blocks per lane" % (shape, mode, rule, fq, tier))
+    assert tier == 20, tier
+    x = W.bits(W.generate("moe", shape))
+    assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq, str(shape))
+
+
+@pytest.mark.parametrize("limit", [0, 1], ids=["never-wait", "one-poll"])
+def test_fused_teams_bounded_wait(nv, orc, limit):
+    shape = (6, 1024, 16384)
+    x = W.bits(W.generate("moe", shape))
+    nv.set_fused_wait_limit(limit)
+    try:
+        say("[fused-teams] wait limit %d" % limit)
+        assert_matches_oracle(orc, x, run_fused(nv, x, "four_over_six", "mse", False),
+                              "four_over_six", "mse", False, "teams-limit%d" % limit)
+    finally:
+        nv.set_fused_wait_limit(-1)
+
+
+def test_fused_teams_moe_full_size(nv, orc):
+    """The 64-expert MoE tensor (2048 x 5120 per expert), read once, whole against the oracle."""
+    shape = W.WORKLOADS["moe"].shape
+    assert nv.fused_blocks_per_lane(shape, "four_over_six", "mse", False) == 20
+    xt = W.generate("moe")
+    say("[fused-teams] moe %s" % (shape,))
+    c, s, a = nv.quantize_fused(xt.cuda(), "four_over_six", "mse")
+    torch.cuda.synchronize()
+    got = dict(codes=c.cpu().numpy(), scales=s.cpu().numpy(), alpha=a.cpu().numpy())
+    del c, s
+    assert_matches_oracle(orc, W.bits(xt), got, "four_over_six", "mse", False, "moe")
 
 
 def test_fused_two_pass_route(nv, orc):
