@@ -20,7 +20,8 @@
 //   fused_kernel     single-read dynamic quantization for tensors that fit on chip: loads
 //                    and keeps each lane's blocks (VGPRs + LDS), reduces amax, waits for
 //                    every workgroup of the tensor at a grid-wide counter, then runs the
-//                    block pass on the blocks it holds
+//                    block pass on the blocks it holds; a batch larger than the chip runs as
+//                    teams of workgroups that take its tensors in turn
 //   dequant_kernel   packed codes + scale bytes + alpha -> bf16, one block per lane
 //
 // All floating-point steps of the encoding are IEEE binary32 with round-to-nearest-even, no
