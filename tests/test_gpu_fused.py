@@ -156,7 +156,9 @@ def test_fused_bounded_wait_fallback(nv, orc, limit, shape):
 TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),
          ((5, 1000, 14336), "four_over_six", "mae", True),
          ((12, 512, 14336), "rtn6", "mse", False),
-         ((3, 2048, 14336), "four_over_six", "maxerr", False)]
+         ((3, 2048, 14336), "four_over_six", "maxerr", False),
+         ((600, 256, 256), "four_over_six", "mse", False),     # one-workgroup teams
+         ((700, 128, 512), "four_over_six", "mae", True)]
 
 
 @pytest.mark.parametrize("shape,mode,rule,fq", TEAMS, ids=["t%d" % i for i in range(len(TEAMS))])
