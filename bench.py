@@ -53,9 +53,10 @@ def log(msg):
 
 
 def source_digest(path: str = KERNEL_SRC) -> str:
-    """First 16 hex digits of the SHA-256 of the kernel source's code: comments removed and
-    runs of white space folded to one space, so that an edit to comments or layout alone
-    keeps the committed counters, and any change to device or host code drops them."""
+    """First 16 hex digits of the SHA-256 of the kernel source's code: comments and white space
+    removed (string and character literals kept as written), so that an edit to comments or
+    layout alone keeps the committed counters, and any change to device or host code drops
+    them."""
     text = open(path, encoding="utf-8").read()
     out, i, n = [], 0, len(text)
     while i < n:
@@ -76,7 +77,7 @@ def source_digest(path: str = KERNEL_SRC) -> str:
         else:
             out.append(c)
             i += 1
-    code = " ".join("".join(out).split())
+    code = "".join("".join(out).split())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 

@@ -966,7 +966,8 @@ __device__ __forceinline__ void fused_tensor(
     if (u < n)
       fused_emit<MODE, RULE, FQ>(held[k][0][tid], held[k][1][tid], u, inT, codesT, scalesT,
                                  outT, tb, n6, n4, alpha, tiny_alpha);
-  }}
+  }
+}
 
 // Grid: x = G workgroups per tensor, y = tensor (TEAMS false), or y = team (TEAMS true): a team
 // of G workgroups takes tensors y, y + gridDim.y, ... in turn.  All workgroups are resident
