@@ -745,12 +745,12 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 //
 // Workspace of one tensor (kFusedWsWords words, zeroed before the launch), one 128-byte line
 // per group so that arrivals and polls spread over many lines.  Workgroup g belongs to group
-// g % S, with S = min(16, max(1, G / 8)) groups of at least 8 workgroups; line i holds the
-// group's max (atomicMax), arrival count and ready flag, and the top line the max and count
-// over the groups.  The workgroup that completes a group forwards the group max to the top
-// line; the one that completes the top line writes (amax | 1) into every group's flag (amax
-// bits have 16 zero low bits), so a poller needs nothing else from memory.  With one group
-// (fewer than 16 workgroups) its completer publishes directly.
+// g % S, with S = min(16, max(1, G / 8)) groups of at least 8 workgroups (one group for up to
+// 16 workgroups); line i holds the group's max (atomicMax), arrival count and ready flag, and
+// the top line the max and count over the groups.  The workgroup that completes a group
+// forwards the group max to the top line; the one that completes the top line writes
+// (amax | 1) into every group's flag (amax bits have 16 zero low bits), so a poller needs
+// nothing else from memory.  With one group its completer publishes directly.
 //
 // All of it is relaxed device-scope atomics: an acquire or release at device scope writes
 // back and invalidates the L2 of the XCD, which at a thousand workgroups cost more than
@@ -881,8 +881,10 @@ __device__ __forceinline__ void fused_tensor(
   if (tid == 0) {
     uint32_t wgm = part[0];
     for (int w = 1; w < kThreads / 64; ++w) wgm = max(wgm, part[w]);
-    // groups of at least 8 workgroups, at most 16 groups; one group needs no top level
-    const uint32_t S = min((uint32_t)kFusedGroups, max(1u, G / 8u));
+    // groups of at least 8 workgroups, at most 16 groups; one group needs no top level.  Up
+    // to 16 workgroups meet on one line (measured 11 % faster for the 16-workgroup 256x256
+    // call); 128 workgroups on one line measured 1.5x slower than 16 groups of 8.
+    const uint32_t S = G <= 16u ? 1u : min((uint32_t)kFusedGroups, max(1u, G / 8u));
     const uint32_t grp = g % S;
     uint32_t* wt = ws + t * kFusedWsWords;
     uint32_t* line = wt + grp * kLineWords;                // [0] max, [1] count, [2] flag
