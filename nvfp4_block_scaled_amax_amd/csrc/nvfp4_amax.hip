@@ -585,10 +585,11 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   // ahead of others and the launch ends with few waves in flight.  With 8 or more steps per
   // lane, each wave lowers its issue priority at a quarter, half and three quarters of its
   // steps, so the waves that are behind are issued first.  (Fewer steps: the hardware's
-  // dispatch of many workgroups balances the load instead.)
+  // dispatch of many workgroups balances the load instead.  The diagnostics variant without
+  // statistics measured 6 % slower paced, so it does not pace.)
   const uint32_t u_first = (uint32_t)__builtin_amdgcn_readfirstlane(u);
   const uint32_t steps = u_first < n ? (n - u_first + stride - 1) / stride : 0;  // wave-uniform
-  const bool pace = steps >= kPacedSteps;
+  const bool pace = steps >= kPacedSteps && (!DIAG || want_stats);
   const uint32_t q1 = steps / 4, q2 = steps / 2, q3 = (3 * steps) / 4;
   if (pace) __builtin_amdgcn_s_setprio(3);
   for (uint32_t step = 0; u < n; u += stride, ++step) {
