@@ -2,10 +2,9 @@
 
 Codes, scale bytes, alpha bits and fake-quant bf16 bits must be identical (the
 arithmetic is binary32 round-to-nearest-even in a fixed order on both sides, so
-the bar is exact equality).  Small tensors are compared whole; the five full-size
-workloads run in the launch configuration the benchmark times and are compared on
-sampled blocks, plus a property that holds at any size (decoding the packed
-output gives the fake-quant output)."""
+the bar is exact equality).  Small tensors and the five full-size workloads (in the
+launch configuration the benchmark times) are compared whole, plus a property that holds
+at any size (decoding the packed output gives the fake-quant output)."""
 from __future__ import annotations
 
 import os
