@@ -313,33 +313,37 @@ __device__ __forceinline__ float fast_candidate(const float (&x)[16], float r, f
 
 // Per-tensor tables in LDS.
 //   D[s] = (d, r): the step d = RN(dec(s) * alpha) of E4M3 byte s and r = RN(1/d) (0 if d = 0)
-//   T[k] = (T6, T4): RN((1 + k/128) / m_Q) where Q*alpha = m_Q * 2^p_Q, m_Q in [0.5, 1).
+//   T[k] = (T6, T4): 2^-p_Q * RN((1 + k/128) / m_Q), where Q*alpha = m_Q * 2^p_Q, m_Q in [0.5, 1).
 // A normal block max is bmax = (1 + k/128) * 2^(e-127) (bf16: 7 fraction bits), so
-// bmax / (Q*alpha) = ((1 + k/128) / m_Q) * 2^(e-127-p_Q), and because rounding to binary32
-// commutes with scaling by a power of two while the result stays normal,
-// RN(bmax / (Q*alpha)) = ldexp(T_Q[k], e-127-p_Q).  Results below 2^-126 become scale byte
-// 0 either way.  This replaces two divisions and two reciprocals per block.
+// bmax / (Q*alpha) = ((1 + k/128) / m_Q) * 2^(e-127-p_Q).  Rounding to binary32 commutes
+// with scaling by a power of two while the result stays normal, so
+// RN(bmax / (Q*alpha)) = T_Q[k] * 2^(e-127), and 2^(e-127) is bmax with its fraction bits
+// cleared: one exact multiply per candidate.  T_Q[k] itself is normal whenever the block pass
+// takes this path (alpha at least 2^-118, and alpha at most FLT_MAX / 1536 because it is
+// amax / (6*M) for a finite amax), so its scaling by 2^-p_Q is exact too.  A product below
+// 2^-126 is below half the least E4M3 subnormal, as is the exact quotient, so both become
+// scale byte 0; one above the binary32 range saturates like the quotient.  This replaces two
+// divisions and two reciprocals per block.
 struct BlockTables {
   f32x2 D[256];
   f32x2 T[128];
 };
 
 template <int MODE>
-__device__ __forceinline__ void build_tables(BlockTables& tb, float alpha, int& n6, int& n4) {
+__device__ __forceinline__ void build_tables(BlockTables& tb, float alpha) {
   const int i = threadIdx.x;
   const float c6 = 6.0f * alpha, c4 = 4.0f * alpha;
   int p6 = 0, p4 = 0;
   const float m6 = frexpf(c6, &p6);
   const float m4 = frexpf(c4, &p4);
-  n6 = 127 + p6;
-  n4 = 127 + p4;
   if (i < 256) {
     const float d = e4m3_to_f32((uint32_t)i & 0x7Fu) * alpha;
     tb.D[i] = f32x2{d, d == 0.0f ? 0.0f : 1.0f / d};
   }
   if (i < 128) {
     const float mk = 1.0f + (float)i * 0.0078125f;
-    tb.T[i] = f32x2{mk / m6, MODE == NVFP4_FOUR_OVER_SIX ? mk / m4 : 0.0f};
+    tb.T[i] = f32x2{__builtin_amdgcn_ldexpf(mk / m6, -p6),
+                    MODE == NVFP4_FOUR_OVER_SIX ? __builtin_amdgcn_ldexpf(mk / m4, -p4) : 0.0f};
   }
 }
 
@@ -347,23 +351,26 @@ __device__ __forceinline__ void build_tables(BlockTables& tb, float alpha, int& 
 // Writes the chosen scale byte s, step d and code words; `slow` marks blocks that must be
 // redone on the reference path.
 template <int MODE, int RULE>
-__device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTables& tb, int n6,
-                                           int n4, bool& slow, uint32_t& s, float& d,
+__device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTables& tb,
+                                           bool& slow, uint32_t& s, float& d,
                                            uint32_t& w0, uint32_t& w1, float& bmax, bool& four) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; i += 2) m = max3_abs(m, x[i], x[i + 1]);
   bmax = m;
   const uint32_t bb = __float_as_uint(m);
-  const int e = (int)(bb >> 23);
   const f32x2 T = tb.T[(bb >> 16) & 0x7Fu];
-  const float sig6 = fminf(__builtin_amdgcn_ldexpf(T.x, e - n6), 448.0f);
-  const float sig4 = MODE == NVFP4_FOUR_OVER_SIX
-                         ? fminf(__builtin_amdgcn_ldexpf(T.y, e - n4), 448.0f) : 0.0f;
+  const float pe = __uint_as_float(bb & 0x7F800000u);   // 2^(e-127)
+  // The E4M3 conversion turns every value above 448 into byte 0x7E or 0x7F (checked on every
+  // input by the hardware-conversion test).  For 4/6 that needs no clamp: the 4-scale is 1.5
+  // times the 6-scale, so whenever either passes 448 the 4-scale byte is 0x7E or above, and
+  // the range check below sends the block to the reference path.  rtn6 clamps at 448.
+  const float sig6 = MODE == NVFP4_FOUR_OVER_SIX ? T.x * pe : fminf(T.x * pe, 448.0f);
+  const float sig4 = MODE == NVFP4_FOUR_OVER_SIX ? T.y * pe : 0.0f;
   const uint32_t sp = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sig6, sig4, 0, false);
   const uint32_t s6 = sp & 0xFFu;
   const f32x2 D6 = tb.D[s6];
-  slow = e == 0;
+  slow = bb < 0x00800000u;   // block max below 2^-126 (or zero)
   four = false;
   const float err6 = fast_candidate<RULE>(x, D6.y, D6.x, w0, w1);
   s = s6;
@@ -372,8 +379,8 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
     const uint32_t s4 = (sp >> 8) & 0xFFu;
     const f32x2 D4 = tb.D[s4];
     // Scaled values can pass 5 (so the cap at FP4 value 4 bites) only when the E4M3 scale
-    // rounded far down: a subnormal byte, or the clamp at 448.  A normal byte is within 1/16
-    // of sigma, so the block max lands at most near 4.27.
+    // rounded far down: a subnormal byte, or a scale past 448 (byte 0x7E or 0x7F).  A normal
+    // byte below 0x7E is within 1/16 of sigma, so the block max lands at most near 4.27.
     slow = slow || (s4 - 8u) >= 0x76u;
     uint32_t a4, b4;
     const float err4 = fast_candidate<RULE>(x, D4.y, D4.x, a4, b4);
@@ -570,8 +577,7 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   LaneStats st = {0.0, 0.0, 0.0, 0.0, 0.0f, 0u};
   const bool want_stats = DIAG && stats != nullptr;
 
-  int n6, n4;
-  build_tables<MODE>(tb, alpha, n6, n4);
+  build_tables<MODE>(tb, alpha);
   __syncthreads();
   const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
 
@@ -608,7 +614,7 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     uint32_t sc, w0, w1;
     float dq, bm;
     bool slow, four;
-    fast_block<MODE, RULE>(x, tb, n6, n4, slow, sc, dq, w0, w1, bm, four);
+    fast_block<MODE, RULE>(x, tb, slow, sc, dq, w0, w1, bm, four);
     if (slow || tiny_alpha) {        // rare: redo the block on the reference path
       const RefOut o =
           ref_block<MODE, RULE>(reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm, alpha);
@@ -790,14 +796,14 @@ __device__ __noinline__ uint32_t wg_tensor_amax(const uint4* __restrict__ p, int
 template <int MODE, int RULE, bool FQ>
 __device__ __forceinline__ void fused_emit(const uint4& c0, const uint4& c1, uint32_t u,
                                            const char* inT, char* codesT, uint8_t* scalesT,
-                                           char* outT, const BlockTables& tb, int n6, int n4,
+                                           char* outT, const BlockTables& tb,
                                            float alpha, bool tiny_alpha) {
   float x[16];
   unpack16(c0, c1, x);
   uint32_t sc, w0, w1;
   float dq, bm;
   bool slow, four;
-  fast_block<MODE, RULE>(x, tb, n6, n4, slow, sc, dq, w0, w1, bm, four);
+  fast_block<MODE, RULE>(x, tb, slow, sc, dq, w0, w1, bm, four);
   if (slow || tiny_alpha) {
     const RefOut o =
         ref_block<MODE, RULE>(reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm, alpha);
@@ -941,8 +947,7 @@ __device__ __forceinline__ void fused_tensor(
     }
     return;
   }
-  int n6, n4;
-  build_tables<MODE>(tb, alpha, n6, n4);
+  build_tables<MODE>(tb, alpha);
   __syncthreads();
   const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
   // Phase 2 is bound by the VALU and every workgroup starts it at once: the waves pace
@@ -957,7 +962,7 @@ __device__ __forceinline__ void fused_tensor(
     if (pace && k == (3 * K) / 4) __builtin_amdgcn_s_setprio(0);
     const uint32_t u = ((uint32_t)k * G + g) * kThreads + tid;
     if (u < n)
-      fused_emit<MODE, RULE, FQ>(r0[k], r1[k], u, inT, codesT, scalesT, outT, tb, n6, n4,
+      fused_emit<MODE, RULE, FQ>(r0[k], r1[k], u, inT, codesT, scalesT, outT, tb,
                                  alpha, tiny_alpha);
   }
 #pragma unroll
@@ -968,7 +973,7 @@ __device__ __forceinline__ void fused_tensor(
     const uint32_t u = ((uint32_t)(KR + k) * G + g) * kThreads + tid;
     if (u < n)
       fused_emit<MODE, RULE, FQ>(held[k][0][tid], held[k][1][tid], u, inT, codesT, scalesT,
-                                 outT, tb, n6, n4, alpha, tiny_alpha);
+                                 outT, tb, alpha, tiny_alpha);
   }
 }
 

@@ -4,6 +4,8 @@
 //     saturating at 6, sign kept; every byte position of the packed word;
 //   - v_cvt_scalef32_pk_f32_fp4 (scale 1): the 16 E2M1 codes to their values;
 //   - v_cvt_pk_fp8_f32 after a clamp at 448: E4M3 (FN) round to nearest even, subnormals kept;
+//   - v_cvt_pk_fp8_f32 without a clamp, above 448 (up to +inf): byte 0x7E or 0x7F in both
+//     positions, which is all the Four Over Six scale pair relies on there;
 //   - v_cvt_pk_bf16_f32: bf16 round to nearest even.
 // Every binary32 bit pattern is tried (NaN inputs excepted; non-negative ones for E4M3, which
 // the block pass only feeds non-negative scales).  Test infrastructure: built beside the tests
@@ -116,6 +118,20 @@ __global__ void fp8_encode_all(uint64_t lo, uint64_t hi, Result* r) {
   tally(r, n);
 }
 
+__global__ void fp8_encode_over(uint64_t lo, uint64_t hi, Result* r) {
+  unsigned long long n = 0;
+  for (uint64_t i = lo + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < hi;
+       i += (uint64_t)gridDim.x * blockDim.x) {
+    const uint32_t u = (uint32_t)i;                // above 448, up to +inf
+    const float s = __uint_as_float(u);
+    const uint32_t hw = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(s, s, 0, false) & 0xFFFFu;
+    const uint32_t b0 = hw & 0xFFu, b1 = hw >> 8;
+    if (b0 < 0x7Eu || b0 > 0x7Fu || b1 < 0x7Eu || b1 > 0x7Fu) record(r, u, hw, 0x7E7Eu);
+    ++n;
+  }
+  tally(r, n);
+}
+
 __global__ void bf16_encode_all(uint64_t lo, uint64_t hi, Result* r) {
   typedef __bf16 b2 __attribute__((ext_vector_type(2)));
   typedef float f2 __attribute__((ext_vector_type(2)));
@@ -135,7 +151,7 @@ __global__ void bf16_encode_all(uint64_t lo, uint64_t hi, Result* r) {
 
 }  // namespace
 
-// which: 0 FP4 encode, 1 FP4 decode, 2 E4M3 encode, 3 bf16 encode.  out[0] = mismatches,
+// which: 0 FP4 encode, 1 FP4 decode, 2 E4M3 encode, 3 bf16 encode, 4 E4M3 above 448.  out[0] = mismatches,
 // out[1..3] = input, hardware and software results of the first one, out[4] = the number of
 // inputs compared.  Returns a hipError_t.
 extern "C" __attribute__((visibility("default"))) int hwconv_check(int which,
@@ -150,6 +166,8 @@ extern "C" __attribute__((visibility("default"))) int hwconv_check(int which,
     else if (which == 1) hipLaunchKernelGGL(fp4_decode_all, dim3(1), dim3(256), 0, 0, d);
     else if (which == 2)
       hipLaunchKernelGGL(fp8_encode_all, dim3(8192), dim3(256), 0, 0, 0ull, 0x7F800001ull, d);
+    else if (which == 4)
+      hipLaunchKernelGGL(fp8_encode_over, dim3(8192), dim3(256), 0, 0, 0x43E00001ull, 0x7F800001ull, d);
     else hipLaunchKernelGGL(bf16_encode_all, dim3(8192), dim3(256), 0, 0, 0ull, all, d);
     e = hipGetLastError();
   }

@@ -17,14 +17,17 @@ pytestmark = pytest.mark.gpu
 
 LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "hw", "libhwconv.so")
 # (which, what, inputs compared): every pattern but NaNs (2 * (2^23 - 1)); 256 bytes x 4
-# positions x 2 codes; +0 up to +inf; every pattern but infinities and NaNs (2 * 2^23).
+# positions x 2 codes; +0 up to +inf; every pattern but infinities and NaNs (2 * 2^23); every
+# pattern above 448 up to +inf.
 CASES = [(0, "v_cvt_scalef32_pk_fp4_f32: E2M1 round to nearest even, all 2^32 inputs, 4 bytes",
           2**32 - 2 * (2**23 - 1)),
          (1, "v_cvt_scalef32_pk_f32_fp4: the 16 codes in each byte position", 256 * 4 * 2),
          (2, "v_cvt_pk_fp8_f32 after the 448 clamp: E4M3 round to nearest even, inputs >= 0",
           0x7F800001),
          (3, "v_cvt_pk_bf16_f32: bf16 round to nearest even, all finite inputs",
-          2**32 - 2 * 2**23)]
+          2**32 - 2 * 2**23),
+         (4, "v_cvt_pk_fp8_f32 with no clamp: every input above 448, up to +inf, gives 0x7E or 0x7F",
+          0x7F800001 - 0x43E00001)]
 
 
 @pytest.fixture(scope="module")
@@ -40,7 +43,7 @@ def hw():
 
 
 @pytest.mark.parametrize("which,what,inputs", CASES,
-                         ids=["fp4-encode", "fp4-decode", "e4m3", "bf16"])
+                         ids=["fp4-encode", "fp4-decode", "e4m3", "bf16", "e4m3-over-448"])
 def test_conversion_matches_definition_on_every_input(hw, which, what, inputs):
     print("[hw] %s" % what, flush=True)
     sys.stdout.flush()
