@@ -56,6 +56,11 @@
 #define NVFP4_AMAX_H
 
 #include <stdint.h>
+/* The library targets AMD GPUs only.  A plain C or C++ compiler (not hipcc) including this
+ * header gets the AMD platform of the HIP runtime API without having to define it. */
+#if !defined(__HIP_PLATFORM_AMD__) && !defined(__HIP_PLATFORM_NVIDIA__)
+#define __HIP_PLATFORM_AMD__ 1
+#endif
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
