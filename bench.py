@@ -284,7 +284,8 @@ def main():
         "config": {"workload": "%s: %s" % (wl.name, wl.description), "shape": list(wl.shape),
                    "elements": N, "mode": args.mode, "rule": args.rule,
                    "output": "fakequant" if fq else "packed", "block": 16,
-                   "rotating_buffer_sets": R, "timed_as": "one HIP graph of K steps"},
+                   "rotating_buffer_sets": R, "timed_as": "one HIP graph of K steps",
+                   "input_sha256": W.sha256(x_cpu)[:16]},
         "roofline": {
             "bound": "hbm", "achieved": round(block_gbps, 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(block_gbps / HBM_PEAK_GBPS, 4),

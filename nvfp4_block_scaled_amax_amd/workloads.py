@@ -27,6 +27,7 @@ small tensors of the same distribution.
 """
 from __future__ import annotations
 
+import hashlib
 import math
 from dataclasses import dataclass
 
@@ -148,3 +149,8 @@ def generate(name: str, shape=None, seed=None) -> torch.Tensor:
 def bits(t: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> numpy uint16 bit patterns (no copy for contiguous CPU tensors)."""
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def sha256(t: torch.Tensor) -> str:
+    """SHA-256 of the tensor's bf16 bytes (row-major), the fingerprint of an input of record."""
+    return hashlib.sha256(memoryview(bits(t).reshape(-1))).hexdigest()
