@@ -223,6 +223,49 @@ def test_fixed_scale_entry(nv, orc, mode, rule):
     assert (ref["scales"] == 0x7E).any()                      # the clamp was exercised
 
 
+# A fixed amax anywhere in the binary32 range, on data of every magnitude: alpha from
+# FLT_MAX / 1536 down to subnormal and zero, across the bound (alpha = 2^-118) below which every
+# block takes the reference path, so the table-driven scales are checked at both ends of the
+# range they claim.
+EXTREME_AMAX = np.array([3.4028235e38, 2.0 ** 120, 1.0e10, 1.0, 1536 * 2.0 ** -118,
+                         np.nextafter(np.float32(1536 * 2.0 ** -118), np.float32(0)),
+                         2688 * 2.0 ** -118,
+                         np.nextafter(np.float32(2688 * 2.0 ** -118), np.float32(1)), 1.0e-30,
+                         1.4e-45, 0.0, -2.0], np.float32)
+
+
+def _extreme_data():
+    rng = np.random.default_rng(21)
+    E = EXTREME_AMAX.size
+    normal = W.bits(W.normal((E * 8, 256), seed=22)).reshape(E, 8, 256)
+    huge = (rng.integers(0x7E00, 0x7F80, size=(E, 8, 256), dtype=np.uint16) |
+            (rng.integers(0, 2, size=(E, 8, 256), dtype=np.uint16) << 15))
+    tiny = (rng.integers(0x0001, 0x0900, size=(E, 8, 256), dtype=np.uint16) |
+            (rng.integers(0, 2, size=(E, 8, 256), dtype=np.uint16) << 15))
+    return {"normal": normal, "huge": huge, "tiny": tiny}
+
+
+@pytest.mark.parametrize("kind", ["normal", "huge", "tiny"])
+@pytest.mark.parametrize("mode,rule", RUNS, ids=["-".join(r) for r in RUNS])
+def test_fixed_scale_extreme_amax(nv, orc, kind, mode, rule):
+    x = _extreme_data()[kind]
+    E = x.shape[0]
+    xg, sg = to_gpu(x), torch.from_numpy(EXTREME_AMAX.copy()).cuda()
+    say("[parity] extreme amax %s %s/%s" % (kind, mode, rule))
+    c, s, a = nv.quantize_from_amax(xg, sg, mode, rule)
+    y, b = nv.fakequant_from_amax(xg, sg, mode, rule)
+    torch.cuda.synchronize()
+    al = np.array([orc.alpha(abs(float(v)), mode) for v in EXTREME_AMAX], np.float32)
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), al.view(np.uint32))
+    assert np.array_equal(b.cpu().numpy().view(np.uint32), al.view(np.uint32))
+    ref = orc.quantize_blocks(x, al, np.arange(x.size // 16), mode, rule)
+    got_s = s.cpu().numpy().ravel()
+    bad = np.nonzero(got_s != ref["scales"])[0]
+    assert bad.size == 0, "scales differ at blocks %s (tensor %s)" % (bad[:4], bad[:4] // (x.size // 16 // E))
+    assert np.array_equal(c.cpu().numpy().reshape(-1, 8), ref["codes"])
+    assert np.array_equal(u16(y).reshape(-1, 16), ref["y"])
+
+
 # ----------------------------------------------------------------------------- in place, guards
 def test_in_place_fakequant(nv, orc):
     x = W.bits(W.generate("act", (64, 512)))
