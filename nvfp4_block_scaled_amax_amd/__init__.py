@@ -120,6 +120,12 @@ def _stream(x: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(x.device).cuda_stream)
 
 
+def _on(x: torch.Tensor):
+    """x's device made current for the call: the library sizes its launches for the current
+    device, and the stream passed is x's device's current stream."""
+    return torch.cuda.device(x.device)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -138,7 +144,8 @@ def amax(x: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
     """Per-tensor max |x| (float32 [E], E = 1 for a 2-D x)."""
     E, rows, cols, _ = _dims(x)
     out = _out(out, (E,), torch.float32, x)
-    _check(lib().nvfp4_amax(_ptr(x), E, rows, cols, _ptr(out), _stream(x)), "nvfp4_amax")
+    with _on(x):
+        _check(lib().nvfp4_amax(_ptr(x), E, rows, cols, _ptr(out), _stream(x)), "nvfp4_amax")
     return out
 
 
@@ -155,12 +162,14 @@ def quantize(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=None, s
     """Packed NVFP4 with a dynamic per-tensor scale -> (codes, scales, alpha)."""
     E, rows, cols, batched = _dims(x)
     codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha)
-    if batched:
-        st = lib().nvfp4_quantize_batched(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
-                                          _ptr(codes), _ptr(scales), _ptr(alpha), _stream(x))
-    else:
-        st = lib().nvfp4_quantize(_ptr(x), rows, cols, BLOCK, _mode(mode), _rule(rule),
-                                  _ptr(codes), _ptr(scales), _ptr(alpha), _stream(x))
+    with _on(x):
+        if batched:
+            st = lib().nvfp4_quantize_batched(_ptr(x), E, rows, cols, BLOCK, _mode(mode),
+                                              _rule(rule), _ptr(codes), _ptr(scales),
+                                              _ptr(alpha), _stream(x))
+        else:
+            st = lib().nvfp4_quantize(_ptr(x), rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                      _ptr(codes), _ptr(scales), _ptr(alpha), _stream(x))
     _check(st, "nvfp4_quantize")
     return codes, scales, alpha
 
@@ -180,10 +189,11 @@ def quantize_diag(x: torch.Tensor, mode="four_over_six", rule="mse", *, stats=Tr
     if stats:
         st_out = torch.empty((E, len(STATS)), dtype=torch.float64, device=x.device)
         ws = _workspace(workspace, diag_ws_words(E), x)
-    st = lib().nvfp4_quantize_diag(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
-                                   _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(qstar),
-                                   _ptr(count4), _ptr(st_out) if stats else None,
-                                   _ptr(ws) if stats else None, _stream(x))
+    with _on(x):
+        st = lib().nvfp4_quantize_diag(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                       _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(qstar),
+                                       _ptr(count4), _ptr(st_out) if stats else None,
+                                       _ptr(ws) if stats else None, _stream(x))
     _check(st, "nvfp4_quantize_diag")
     return codes, scales, alpha, qstar, count4, st_out
 
@@ -194,12 +204,13 @@ def fakequant(x: torch.Tensor, mode="four_over_six", rule="mse", *, out=None, al
     E, rows, cols, batched = _dims(x)
     out = _out(out, x.shape, torch.bfloat16, x)
     alpha = _out(alpha, (E,), torch.float32, x)
-    if batched:
-        st = lib().nvfp4_fakequant_batched(_ptr(x), E, rows, cols, BLOCK, _mode(mode),
-                                           _rule(rule), _ptr(out), _ptr(alpha), _stream(x))
-    else:
-        st = lib().nvfp4_fakequant(_ptr(x), rows, cols, BLOCK, _mode(mode), _rule(rule),
-                                   _ptr(out), _ptr(alpha), _stream(x))
+    with _on(x):
+        if batched:
+            st = lib().nvfp4_fakequant_batched(_ptr(x), E, rows, cols, BLOCK, _mode(mode),
+                                               _rule(rule), _ptr(out), _ptr(alpha), _stream(x))
+        else:
+            st = lib().nvfp4_fakequant(_ptr(x), rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                       _ptr(out), _ptr(alpha), _stream(x))
     _check(st, "nvfp4_fakequant")
     return out, alpha
 
@@ -210,9 +221,10 @@ def quantize_from_amax(x: torch.Tensor, amax_: torch.Tensor, mode="four_over_six
     E, rows, cols, batched = _dims(x)
     amax_ = _out(amax_, (E,), torch.float32, x)
     codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha)
-    st = lib().nvfp4_quantize_from_amax(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
-                                        _ptr(amax_), _ptr(codes), _ptr(scales), _ptr(alpha),
-                                        _stream(x))
+    with _on(x):
+        st = lib().nvfp4_quantize_from_amax(_ptr(x), E, rows, cols, BLOCK, _mode(mode),
+                                            _rule(rule), _ptr(amax_), _ptr(codes), _ptr(scales),
+                                            _ptr(alpha), _stream(x))
     _check(st, "nvfp4_quantize_from_amax")
     return codes, scales, alpha
 
@@ -224,8 +236,10 @@ def fakequant_from_amax(x: torch.Tensor, amax_: torch.Tensor, mode="four_over_si
     amax_ = _out(amax_, (E,), torch.float32, x)
     out = _out(out, x.shape, torch.bfloat16, x)
     alpha = _out(alpha, (E,), torch.float32, x)
-    st = lib().nvfp4_fakequant_from_amax(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
-                                         _ptr(amax_), _ptr(out), _ptr(alpha), _stream(x))
+    with _on(x):
+        st = lib().nvfp4_fakequant_from_amax(_ptr(x), E, rows, cols, BLOCK, _mode(mode),
+                                             _rule(rule), _ptr(amax_), _ptr(out), _ptr(alpha),
+                                             _stream(x))
     _check(st, "nvfp4_fakequant_from_amax")
     return out, alpha
 
@@ -246,8 +260,9 @@ def dequantize(codes: torch.Tensor, scales: torch.Tensor, alpha: torch.Tensor, *
     if tuple(scales.shape) != tuple(codes.shape[:-1]) + (cols // 16,) or alpha.numel() != E:
         raise ValueError("scales must be [..., rows, cols/16] and alpha [E]")
     out = _out(out, tuple(codes.shape[:-1]) + (cols,), torch.bfloat16, codes)
-    _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(alpha), E, rows, cols,
-                                  _ptr(out), _stream(codes)), "nvfp4_dequantize")
+    with _on(codes):
+        _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(alpha), E, rows, cols,
+                                      _ptr(out), _stream(codes)), "nvfp4_dequantize")
     return out
 
 
@@ -270,8 +285,10 @@ def quantize_fused(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=N
     E, rows, cols, batched = _dims(x)
     codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha)
     ws = _workspace(workspace, FUSED_WS_WORDS * E, x)
-    st = lib().nvfp4_quantize_fused(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
-                                    _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(ws), _stream(x))
+    with _on(x):
+        st = lib().nvfp4_quantize_fused(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
+                                        _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(ws),
+                                        _stream(x))
     _check(st, "nvfp4_quantize_fused")
     return codes, scales, alpha
 
@@ -284,8 +301,10 @@ def fakequant_fused(x: torch.Tensor, mode="four_over_six", rule="mse", *, out=No
     out = _out(out, x.shape, torch.bfloat16, x)
     alpha = _out(alpha, (E,), torch.float32, x)
     ws = _workspace(workspace, FUSED_WS_WORDS * E, x)
-    st = lib().nvfp4_fakequant_fused(_ptr(x), E, rows, cols, BLOCK, _mode(mode), _rule(rule),
-                                     _ptr(out), _ptr(alpha), _ptr(ws), _stream(x))
+    with _on(x):
+        st = lib().nvfp4_fakequant_fused(_ptr(x), E, rows, cols, BLOCK, _mode(mode),
+                                         _rule(rule), _ptr(out), _ptr(alpha), _ptr(ws),
+                                         _stream(x))
     _check(st, "nvfp4_fakequant_fused")
     return out, alpha
 
