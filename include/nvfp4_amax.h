@@ -209,8 +209,9 @@ nvfp4_status nvfp4_fakequant_fused(const uint16_t* in, int64_t E, int64_t rows, 
                                    float* out_alpha, uint32_t* workspace, hipStream_t stream);
 
 /* For a fused call of this shape, mode, rule and output form on the current device: the
- * number of blocks each lane holds on chip (1, 4, 12 or 28) if it reads its input once, 0 if
- * it takes the two-pass path, or minus a status code for bad arguments.  On MI355X up to
+ * most blocks a lane holds on chip (1, 4, 12 or 28; a tensor spread over more workgroups
+ * leaves each lane fewer) if it reads its input once, 0 if it takes the two-pass path, or
+ * minus a status code for bad arguments.  On MI355X up to
  * 3,670,016 blocks per launch (E * rows * cols / 16; 117 MB of bf16) are held at once.  A larger
  * batch whose single tensors fit (up to 2,621,440 blocks each) is read once too, by teams of
  * workgroups that take its tensors in turn: the call then returns 20. */

@@ -774,6 +774,7 @@ constexpr uint32_t kFusedMaxWaitLimit = 1u << 26;       // the most a caller may
 // workgroups per CU measured best on the 64-expert MoE batch (24: no gain over two passes,
 // 16: slower); 12 leaves the registers that the loop over tensors needs without spilling.
 constexpr int kTeamKR = 12;
+constexpr int64_t kFusedMaxTensorWGs = 512;           // see fused_tier_wgs
 constexpr int kFusedGroups = 16;
 constexpr int kLineWords = 32;                           // 128 bytes
 constexpr int64_t kFusedWsWords = (kFusedGroups + 1) * kLineWords;
@@ -1325,7 +1326,14 @@ int64_t fused_resident_wgs() {
 
 // Workgroups per tensor G and teams T for one tier: T = E when every tensor fits on chip at
 // once (TEAMS false), else (TEAMS true) as many teams as are resident together, when at least
-// one is; T = 0 when the tier does not fit.  Teams are widened to fill every resident slot:
+// one is; T = 0 when the tier does not fit.
+//   - An all-at-once tier is taken only with at most kFusedMaxTensorWGs workgroups per tensor:
+//     beyond that the 16 counter lines of the grid-wide wait take more than 32 arrivals each.
+//     Measured on an 8192x4096 tensor, 4/6-MSE packed: the 4-block tier with 2048 workgroups
+//     48.5 us, the 28-block tier with 512 workgroups 34.4 us; rtn6 40.5 against 26.5 us.
+//   - The 12- and 28-block tiers spread each tensor over resident / E workgroups (fewer blocks
+//     per lane): 2-8 % faster on the tensors and batches measured.
+//   - Teams are widened to fill every resident slot:
 // a team holds one tensor with at least G workgroups, and with T teams each gets resident / T
 // (fewer blocks per lane).  Measured against teams of exactly G: 18-20 % faster on batches of
 // 524,288-block tensors (where 4 teams of 103 workgroups left 100 of 512 slots idle), 6-9 %
@@ -1336,8 +1344,8 @@ int64_t fused_tier_wgs(const Shape& s, int64_t* teams) {
   const int64_t G = (s.nblk + per_wg - 1) / per_wg;
   const int64_t resident = fused_resident_wgs<MODE, RULE, FQ, KR, KL, TEAMS>();
   if (!TEAMS) {
-    *teams = G * s.E <= resident ? s.E : 0;
-    return G;
+    *teams = (G * s.E <= resident && G <= kFusedMaxTensorWGs) ? s.E : 0;
+    return (KR + KL >= 12 && *teams > 0) ? std::max(G, resident / s.E) : G;
   }
   const int64_t T = std::min(s.E, resident / G);
   *teams = T;

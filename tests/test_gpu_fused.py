@@ -87,7 +87,7 @@ def test_fused_random_shapes(nv, orc):
 
 
 # Shapes that select each tier on a 256-CU MI355X (the test checks the tier it gets).
-TIERS = [(1, (256, 256)), (4, (1024, 8208)), (12, (4096, 8448)), (28, (4096, 14336))]
+TIERS = [(1, (256, 256)), (4, (1024, 4112)), (12, (4096, 4112)), (28, (4096, 14336))]
 
 
 @pytest.mark.parametrize("tier,shape", TIERS, ids=["tier%d" % t for t, _ in TIERS])
@@ -135,7 +135,7 @@ def test_fused_poison_only_its_tensor(nv, orc):
 
 
 @pytest.mark.parametrize("limit", [0, 1], ids=["never-wait", "one-poll"])
-@pytest.mark.parametrize("shape", [(5, 130, 320), (1024, 8208), (4096, 8448)],
+@pytest.mark.parametrize("shape", [(5, 130, 320), (1024, 4112), (4096, 4112)],
                          ids=["batched", "tier4", "tier12"])
 def test_fused_bounded_wait_fallback(nv, orc, limit, shape):
     """The wait for the other workgroups is cut short from the host: workgroups that stop
