@@ -558,6 +558,12 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   const uint32_t n = (uint32_t)nblk;
   const uint32_t stride = gridDim.x * kThreads;
   uint32_t u = blockIdx.x * kThreads + threadIdx.x;
+  // the first block's loads go out before the tables are built (they do not depend on alpha)
+  uint4 nx0 = make_uint4(0u, 0u, 0u, 0u), nx1 = nx0;
+  if (u < n) {
+    nx0 = *reinterpret_cast<const uint4*>(inT + (u << 5));
+    nx1 = *reinterpret_cast<const uint4*>(inT + (u << 5) + 16);
+  }
 
   if (poison) {                                  // non-finite input or amax
     if (DIAG && stats && blockIdx.x == 0 && threadIdx.x == 0)
@@ -583,11 +589,6 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   __syncthreads();
   const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
 
-  uint4 nx0 = make_uint4(0u, 0u, 0u, 0u), nx1 = nx0;
-  if (u < n) {
-    nx0 = *reinterpret_cast<const uint4*>(inT + (u << 5));
-    nx1 = *reinterpret_cast<const uint4*>(inT + (u << 5) + 16);
-  }
   // Waves that start together on a SIMD do not progress together: issue goes to the oldest
   // ready wave, so in a grid that strides over many blocks per lane some waves finish far
   // ahead of others and the launch ends with few waves in flight.  With 8 or more steps per
