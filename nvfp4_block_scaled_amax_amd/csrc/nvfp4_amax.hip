@@ -1344,11 +1344,11 @@ int64_t fused_resident_wgs() {
 //     48.5 us, the 28-block tier with 512 workgroups 34.4 us; rtn6 40.5 against 26.5 us.
 //   - The 12- and 28-block tiers spread each tensor over resident / E workgroups (fewer blocks
 //     per lane): 2-8 % faster on the tensors and batches measured.
-//   - Teams are widened to fill every resident slot:
-// a team holds one tensor with at least G workgroups, and with T teams each gets resident / T
-// (fewer blocks per lane).  Measured against teams of exactly G: 18-20 % faster on batches of
-// 524,288-block tensors (where 4 teams of 103 workgroups left 100 of 512 slots idle), 6-9 %
-// on 262,144- and 1,048,576-block tensors.
+//   - Teams are widened to fill every resident slot: a team holds one tensor with at least G
+//     workgroups, and with T teams each gets resident / T (fewer blocks per lane).  Measured
+//     against teams of exactly G: 18-20 % faster on batches of 524,288-block tensors (where 4
+//     teams of 103 workgroups left 100 of 512 slots idle), 6-9 % on 262,144- and
+//     1,048,576-block tensors.
 template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS>
 int64_t fused_tier_wgs(const Shape& s, int64_t* teams) {
   constexpr int64_t per_wg = (int64_t)(KR + KL) * kThreads;
