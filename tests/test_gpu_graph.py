@@ -99,3 +99,41 @@ def test_graph_replays_match_eager(nv, orc, shape, mode, rule):
     assert np.array_equal(W.bits(y.cpu()), o["y"])
     assert torch.equal(codes3, codes) and torch.equal(y3, y) and torch.equal(alpha3, alpha)
     assert torch.equal(codes4, codes) and torch.equal(scales4, scales)
+
+
+@pytest.mark.parametrize("shape,fq", [((600, 256, 256), False), ((4096, 4112), True),
+                                      ((6, 1024, 16384), False)],
+                         ids=["teams-small", "tier12-fq", "teams-large"])
+def test_graph_replays_of_fused_tiers_and_teams(nv, shape, fq):
+    """The single-read call in its spread tiers and in team mode, captured and replayed: every
+    replay equals the eager two-pass result."""
+    x = W.generate("moe" if len(shape) == 3 else "weight", shape).cuda()
+    E = shape[0] if len(shape) == 3 else 1
+    lead = shape[:-2]
+    ws = torch.empty(nv.FUSED_WS_WORDS * E, dtype=torch.int32, device="cuda")
+    if fq:
+        out, al = torch.empty_like(x), torch.empty(E, dtype=torch.float32, device="cuda")
+        ref = nv.fakequant(x, "four_over_six", "mse")
+        outs = (out, al)
+        work = lambda: nv.fakequant_fused(x, "four_over_six", "mse", out=out, alpha=al, workspace=ws)
+    else:
+        c = torch.empty(lead + (shape[-2], shape[-1] // 2), dtype=torch.uint8, device="cuda")
+        s = torch.empty(lead + (shape[-2], shape[-1] // 16), dtype=torch.uint8, device="cuda")
+        al = torch.empty(E, dtype=torch.float32, device="cuda")
+        ref = nv.quantize(x, "four_over_six", "mse")
+        outs = (c, s, al)
+        work = lambda: nv.quantize_fused(x, "four_over_six", "mse", codes=c, scales=s, alpha=al,
+                                         workspace=ws)
+    torch.cuda.synchronize()
+    print("[graph] fused %s fq=%s: %d blocks per lane" % (
+        shape, fq, nv.fused_blocks_per_lane(shape, "four_over_six", "mse", fq)), flush=True)
+    assert nv.fused_blocks_per_lane(shape, "four_over_six", "mse", fq) > 0
+    g = _capture(work)
+    for r in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (t, e) in enumerate(zip(outs, ref)):
+            assert torch.equal(t.view(torch.uint8), e.view(torch.uint8)), (r, k)
