@@ -188,7 +188,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //   2048 workgroups, 8 or 16 blocks per lane, 2048 or 4096 workgroups for long launches, and
 //   1024-4096 workgroups for rtn6 and fake-quant were all slower or equal.  For long launches
 //   2 or 6 blocks per lane were slower too; 3 measured 2-3 % faster on one box and 1-3 %
-//   slower on another, which is within the spread between boxes.
+//   slower on another, which is within the spread between boxes.  With the first loads issued
+//   at the kernel's start, 768, 1536 and 2048 workgroups measured 1-7 % slower than 1024 on
+//   the 4096x14336 weight.
 constexpr int64_t kLongLaunchBlocks = INT64_C(1) << 23;
 constexpr int64_t kShortLaunchWGs = 1024;
 constexpr int64_t kLaneBlocksLong = 4;
