@@ -782,15 +782,18 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 constexpr uint32_t kFusedDefaultWaitLimit = 1u << 20;   // polls of ~1 us (a device-scope load
                                                          // and a short sleep): about 1 s
 constexpr uint32_t kFusedMaxWaitLimit = 1u << 26;       // the most a caller may set: ~1 min
-// Blocks per lane held in VGPRs in team launches (plus 8 in LDS).  20 per lane with two
-// workgroups per CU measured best on the 64-expert MoE batch (24: no gain over two passes,
-// 16: slower); 12 leaves the registers that the loop over tensors needs without spilling.
-constexpr int kTeamKR = 12;
+// Blocks per lane in team launches: kTeamKR in VGPRs plus kTeamKL in LDS.  20 per lane with
+// two workgroups per CU measured best on the 64-expert MoE batch (24: no gain over two passes,
+// 16: slower).  16 + 4 leaves the registers that the loop over tensors needs without spilling
+// (20 in VGPRs would spill) and measured 1-5 % faster than 12 + 8 (MoE 4/6-MSE 430-445
+// against 454-470 us).
+constexpr int kTeamKR = 16;
+constexpr int kTeamKL = 4;
 constexpr int64_t kFusedMaxTensorWGs = 512;           // see fused_tier_wgs
 // Teams of tensors under this many blocks hold 12 blocks per lane in VGPRs and none in LDS, so
 // that more workgroups fit per CU: 600 tensors of 256x256, 4/6-MSE, 39.0 against 47.2 us;
 // 64 of 1024x2048 105.3 against 115.5 us.  From 262,144 blocks on, 12 + 8 measured equal or
-// faster (the 64-expert MoE batch: 452 against 526 us).
+// faster (the 64-expert MoE batch: 452 against 526 us, with 12 + 8).
 constexpr int64_t kTeamSmallBlocks = INT64_C(1) << 18;
 constexpr int kFusedGroups = 16;
 constexpr int kLineWords = 32;                           // 128 bytes
@@ -1409,7 +1412,7 @@ int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uin
   if (s.nblk < kTeamSmallBlocks) {
     NVFP4_FUSED_TIER(12, 0, true)
   }
-  NVFP4_FUSED_TIER(kTeamKR, 8, true)
+  NVFP4_FUSED_TIER(kTeamKR, kTeamKL, true)
 #undef NVFP4_FUSED_TIER
   return 0;
 }
