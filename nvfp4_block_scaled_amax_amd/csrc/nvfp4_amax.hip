@@ -784,11 +784,11 @@ constexpr uint32_t kFusedDefaultWaitLimit = 1u << 20;   // polls of ~1 us (a dev
 constexpr uint32_t kFusedMaxWaitLimit = 1u << 26;       // the most a caller may set: ~1 min
 // Blocks per lane in team launches: kTeamKR in VGPRs plus kTeamKL in LDS.  20 per lane with
 // two workgroups per CU measured best on the 64-expert MoE batch (24: no gain over two passes,
-// 16: slower).  16 + 4 leaves the registers that the loop over tensors needs without spilling
-// (20 in VGPRs would spill) and measured 1-5 % faster than 12 + 8 (MoE 4/6-MSE 430-445
-// against 454-470 us).
-constexpr int kTeamKR = 16;
-constexpr int kTeamKL = 4;
+// 16: slower).  18 + 2 leaves the registers that the loop over tensors needs without spilling
+// (20 in VGPRs would spill).  On the MoE batch, 4/6-MSE: 12 + 8 454-470 us, 16 + 4 430-445 us,
+// 18 + 2 429-437 us (16 + 4 and 18 + 2 equal on the other batches measured).
+constexpr int kTeamKR = 18;
+constexpr int kTeamKL = 2;
 constexpr int64_t kFusedMaxTensorWGs = 512;           // see fused_tier_wgs
 // Teams of tensors under this many blocks hold 12 blocks per lane in VGPRs and none in LDS, so
 // that more workgroups fit per CU: 600 tensors of 256x256, 4/6-MSE, 39.0 against 47.2 us;
