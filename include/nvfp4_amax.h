@@ -214,7 +214,7 @@ nvfp4_status nvfp4_fakequant_fused(const uint16_t* in, int64_t E, int64_t rows, 
  * minus a status code for bad arguments.  On MI355X up to
  * 3,670,016 blocks per launch (E * rows * cols / 16; 117 MB of bf16) are held at once.  A larger
  * batch whose single tensors fit (up to 2,621,440 blocks each) is read once too, by teams of
- * workgroups that take its tensors in turn: the call then returns 20 (12 for tensors under
+ * workgroups that take its tensors in turn: the call then returns 20 (10 for tensors under
  * 262,144 blocks). */
 int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols, nvfp4_mode mode,
                             nvfp4_rule rule, int fakequant);

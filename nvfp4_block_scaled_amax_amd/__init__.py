@@ -311,7 +311,7 @@ def fakequant_fused(x: torch.Tensor, mode="four_over_six", rule="mse", *, out=No
 
 def fused_blocks_per_lane(shape, mode="four_over_six", rule="mse", fakequant=False) -> int:
     """Most blocks a lane holds on chip in a fused call of this shape (1, 4, 12 or 28; 20 for a
-    batch read by teams of workgroups that take its tensors in turn, 12 when those tensors have
+    batch read by teams of workgroups that take its tensors in turn, 10 when those tensors have
     under 262,144 blocks), or 0 when the call takes the two-pass path (on the current device)."""
     shape = tuple(shape)
     if len(shape) not in (2, 3):

@@ -790,11 +790,13 @@ constexpr uint32_t kFusedMaxWaitLimit = 1u << 26;       // the most a caller may
 constexpr int kTeamKR = 18;
 constexpr int kTeamKL = 2;
 constexpr int64_t kFusedMaxTensorWGs = 512;           // see fused_tier_wgs
-// Teams of tensors under this many blocks hold 12 blocks per lane in VGPRs and none in LDS, so
-// that more workgroups fit per CU: 600 tensors of 256x256, 4/6-MSE, 39.0 against 47.2 us;
-// 64 of 1024x2048 105.3 against 115.5 us.  From 262,144 blocks on, 12 + 8 measured equal or
-// faster (the 64-expert MoE batch: 452 against 526 us, with 12 + 8).
+// Teams of tensors under kTeamSmallBlocks blocks hold kTeamSmallKR blocks per lane in VGPRs
+// and none in LDS, so that more workgroups fit per CU.  4/6-MSE against 12 + 8: 600 tensors of
+// 256x256 38.9 against 47.2 us; 128 of 1024x1024 96.1 against 108.8 us (12 per lane: 107.7;
+// 8 per lane: 95.7, but rtn6 fake-quant up to 4 % slower than 10).  From 262,144 blocks on,
+// the larger team tier measured equal or faster (the 64-expert MoE batch: 452 against 526 us).
 constexpr int64_t kTeamSmallBlocks = INT64_C(1) << 18;
+constexpr int kTeamSmallKR = 10;
 constexpr int kFusedGroups = 16;
 constexpr int kLineWords = 32;                           // 128 bytes
 constexpr int64_t kFusedWsWords = (kFusedGroups + 1) * kLineWords;
@@ -1410,7 +1412,7 @@ int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uin
   NVFP4_FUSED_TIER(12, 0, false)
   NVFP4_FUSED_TIER(20, 8, false)
   if (s.nblk < kTeamSmallBlocks) {
-    NVFP4_FUSED_TIER(12, 0, true)
+    NVFP4_FUSED_TIER(kTeamSmallKR, 0, true)
   }
   NVFP4_FUSED_TIER(kTeamKR, kTeamKL, true)
 #undef NVFP4_FUSED_TIER

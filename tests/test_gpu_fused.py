@@ -152,7 +152,7 @@ def test_fused_bounded_wait_fallback(nv, orc, limit, shape):
 
 
 # Batches that no tier holds at once but whose single tensors fit: teams of workgroups take the
-# tensors in turn (20 blocks per lane, 12 for tensors under 262,144 blocks; odd teams start half
+# tensors in turn (20 blocks per lane, 10 for tensors under 262,144 blocks; odd teams start half
 # a cycle late).
 TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),
          ((5, 1000, 14336), "four_over_six", "mae", True),
@@ -166,7 +166,7 @@ TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),
 def test_fused_teams_whole_batch(nv, orc, shape, mode, rule, fq):
     tier = nv.fused_blocks_per_lane(shape, mode, rule, fq)
     say("[fused-teams] %s %s/%s fq=%s: %d blocks per lane" % (shape, mode, rule, fq, tier))
-    assert tier == (12 if shape[1] * shape[2] // 16 < 2 ** 18 else 20), tier
+    assert tier == (10 if shape[1] * shape[2] // 16 < 2 ** 18 else 20), tier
     x = W.bits(W.generate("moe", shape))
     assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq, str(shape))
 
