@@ -39,8 +39,9 @@
  * E = 1 for the non-batched calls.
  *
  * Ownership and ordering: every pointer is a device pointer owned by the caller.  The
- * library allocates nothing and keeps no state (apart from a test setting and a per-device
- * cache of occupancy figures); calls are reentrant.  All work is
+ * library allocates nothing.  Its only process-wide state is the wait limit of the
+ * single-read calls (a test setting) and a per-device cache of occupancy figures, both
+ * read and written atomically; calls are reentrant.  All work is
  * enqueued on `stream` (0 = the null stream) and the call returns at once; outputs are
  * defined once the stream passes the call.  During a dynamic-scale call out_alpha holds
  * the running amax, so it must not alias any other argument.  Fake-quant may run in
@@ -67,7 +68,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 4
+#define NVFP4_ABI_VERSION 5
 #define NVFP4_BLOCK 16
 
 typedef enum { NVFP4_RTN6 = 0, NVFP4_FOUR_OVER_SIX = 1 } nvfp4_mode;
@@ -82,8 +83,9 @@ typedef enum {
   NVFP4_ERR_BLOCK = 3,  /* block != 16 */
   NVFP4_ERR_ENUM = 4,   /* mode or rule out of range */
   NVFP4_ERR_ALIGN = 5,  /* in/out/codes not 16-byte aligned, alpha/amax not 4-byte */
-  NVFP4_ERR_ALIAS = 6,  /* overlapping arguments (other than in-place fake-quant) */
-  NVFP4_ERR_HIP = 7     /* a kernel launch failed */
+  NVFP4_ERR_HIP = 6,    /* a kernel launch failed */
+  NVFP4_ERR_ALIAS = 7   /* overlapping arguments (other than in-place fake-quant); added
+                           after the first six, so it takes the next free number */
 } nvfp4_status;
 
 /* ABI version (NVFP4_ABI_VERSION) and a static description of a status code. */
@@ -97,21 +99,31 @@ const char* nvfp4_status_str(nvfp4_status status);
 nvfp4_status nvfp4_amax(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
                         float* out_amax, hipStream_t stream);
 
-/* Packed NVFP4 quantization with a dynamic per-tensor scale: amax pass, then the block
- * pass (both candidates and the selection in registers), then alpha is written.
+/* Packed NVFP4 quantization with a dynamic per-tensor scale.  Each block of 16 values gets
+ * one E4M3 scale and 16 FP4 codes; under Four Over Six each block is quantized twice, with
+ * its max mapped to 6 and to 4, and the candidate with the smaller error (rule: MSE, MAE or
+ * max error, against the original values) is kept (Four Over Six explainer, "Method / core
+ * mechanism" and "Adaptive block scaling algorithm"; the per-tensor scale with 448 or 256,
+ * "Implementation details").  Launches: amax pass, then the block pass (both candidates and
+ * the selection in registers), then alpha is written.
  * out_codes [rows][cols/2], out_scales [rows][cols/16], out_alpha [1]. */
 nvfp4_status nvfp4_quantize(const uint16_t* in, int64_t rows, int64_t cols, int block,
                             nvfp4_mode mode, nvfp4_rule rule, uint8_t* out_codes,
                             uint8_t* out_scales, float* out_alpha, hipStream_t stream);
 
 /* Simulated quantization: out = bf16(dequantize(quantize(in))), bit-identical to decoding
- * the packed result of nvfp4_quantize.  out may equal in. */
+ * the packed result of nvfp4_quantize.  The QAD student forward runs through this op
+ * (Nemotron 3.5 Lightning NVFP4 news page, "two-stage QAD"; the Model Optimizer blog's QAD
+ * section); the encoding is the one of nvfp4_quantize.  out may equal in.  out [rows][cols]
+ * bf16, out_alpha [1]. */
 nvfp4_status nvfp4_fakequant(const uint16_t* in, int64_t rows, int64_t cols, int block,
                              nvfp4_mode mode, nvfp4_rule rule, uint16_t* out,
                              float* out_alpha, hipStream_t stream);
 
-/* E independent tensors [E][rows][cols] in one launch per pass, one alpha per tensor
- * (e.g. the experts of a mixture-of-experts layer). */
+/* E independent tensors [E][rows][cols] in one launch per pass, one alpha per tensor: the
+ * per-tensor scale of the Four Over Six explainer ("Implementation details") taken per
+ * tensor of the batch, e.g. per expert of a mixture-of-experts layer (the Model Optimizer
+ * blog quantizes an MoE model).  Outputs as above with a leading [E]; out_alpha [E]. */
 nvfp4_status nvfp4_quantize_batched(const uint16_t* in, int64_t E, int64_t rows,
                                     int64_t cols, int block, nvfp4_mode mode,
                                     nvfp4_rule rule, uint8_t* out_codes,
@@ -195,9 +207,13 @@ nvfp4_status nvfp4_quantize_diag(const uint16_t* in, int64_t E, int64_t rows, in
  * fake-quant (out == in), take the two-pass path instead, with the same results; the
  * workspace is then unused.  All workgroups of a
  * single-read launch must be resident together; the grid is sized for that from the
- * device's occupancy.  Their wait for each other is bounded: a workgroup that waits too long
- * (for instance while other fused calls hold the CUs) computes the tensor amax itself from
- * the input, so the call always completes with the same result.  Errors as above, plus
+ * device's occupancy.  Their wait for each other is bounded in time by the work: 8 times the
+ * launch's expected load time (the bytes loaded at once, at 4 TB/s) plus 50 us, on the
+ * device's constant-rate wall clock.  A workgroup that waits longer (for instance while other
+ * kernels hold the CUs) computes the tensor amax itself from the input, so the call always
+ * completes with the same result, at the cost of that extra read.  Two fused calls that run
+ * concurrently (different streams or graph branches) can each leave part of their workgroups
+ * unplaced and then take that slow path.  Errors as above, plus
  * NVFP4_ERR_NULL for a null workspace and NVFP4_ERR_ALIAS when it overlaps another argument. */
 #define NVFP4_FUSED_WS_WORDS 544   /* workspace words per tensor of the fused calls */
 nvfp4_status nvfp4_quantize_fused(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
@@ -219,10 +235,10 @@ nvfp4_status nvfp4_fakequant_fused(const uint16_t* in, int64_t E, int64_t rows, 
 int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols, nvfp4_mode mode,
                             nvfp4_rule rule, int fakequant);
 
-/* Test hook (process-wide, the library's only setting): how many times a workgroup of a
- * single-read launch polls for the other workgroups (about 1 us each) before it computes
- * the tensor amax itself.  0 = never wait; a negative value restores the default (2^20);
- * larger values are capped at 2^26, so that a wait always ends. */
+/* Test hook (process-wide, the library's only setting): at most how many times a workgroup
+ * of a single-read launch polls for the other workgroups before it computes the tensor amax
+ * itself; the time bound above applies as well.  0 = never wait; a negative value restores
+ * the default (2^26 polls, so that the time bound governs); larger values are capped at 2^26. */
 void nvfp4_fused_set_wait_limit(int64_t polls);
 
 /* Dequantize packed NVFP4 to bf16 (for W4A16-style consumers that store 4-bit weights; the

@@ -38,7 +38,7 @@ class NVFP4Error(RuntimeError):
 
 
 _lib = None
-ABI_VERSION = 4                  # NVFP4_ABI_VERSION of include/nvfp4_amax.h
+ABI_VERSION = 5                  # NVFP4_ABI_VERSION of include/nvfp4_amax.h
 FUSED_WS_WORDS = 544             # NVFP4_FUSED_WS_WORDS: workspace int32 words per tensor
 
 
