@@ -598,7 +598,7 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 
   build_tables<MODE>(tb, alpha);
   __syncthreads();
-  const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
+  const bool tiny_alpha = alpha < 0x1p-118f;   // 1/d may overflow below 2^-118
 
   // Waves that start together on a SIMD do not progress together: issue goes to the oldest
   // ready wave, so in a grid that strides over many blocks per lane some waves finish far
@@ -761,8 +761,11 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 // workgroups of a tensor then meet at a two-level counter in the caller's workspace; the last
 // to arrive publishes amax, and each workgroup runs the block pass on the blocks it holds.
 // The host sizes the grid so that every workgroup can be resident at once.  The wait is
-// bounded: after `wait_limit` polls a workgroup computes the tensor amax itself from the input
-// (the same exact value), so every wave exits whatever the scheduling.
+// bounded: after `wait_polls` polls or `wait_ticks` ticks of the device's constant-rate wall
+// clock, whichever comes first, a workgroup computes the tensor amax itself from the input (the
+// same exact value), so every wave exits whatever the scheduling.  The host derives the time
+// bound from the work (a small multiple of the launch's expected load time), so that a
+// workgroup kept waiting by CUs held elsewhere gives up after a few hundred microseconds.
 //
 // Workspace of one tensor (kFusedWsWords words, zeroed before the launch), one 128-byte line
 // per group so that arrivals and polls spread over many lines.  Workgroup g belongs to group
@@ -779,9 +782,14 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 // issuing the count only after the returning atomicMax is back (a register dependency on its
 // result).  A group's completer reads the group max only after its own count returned, so
 // every member's max is in; the top level works the same way.
-constexpr uint32_t kFusedDefaultWaitLimit = 1u << 20;   // polls of ~1 us (a device-scope load
-                                                         // and a short sleep): about 1 s
-constexpr uint32_t kFusedMaxWaitLimit = 1u << 26;       // the most a caller may set: ~1 min
+constexpr uint32_t kFusedMaxWaitPolls = 1u << 26;   // the poll cap (the default); each poll is
+                                                     // a device-scope load and a short sleep
+// Time bound of every wait of a launch: kWaitFactor times the launch's expected load time (the
+// bytes its resident workgroups load at once, at kWaitLoadRate bytes per microsecond, below the
+// device-copy rate measured on MI355X) plus kWaitFloorUs.
+constexpr double kWaitFactor = 8.0;
+constexpr double kWaitLoadRate = 4.0e6;   // bytes per microsecond: 4 TB/s
+constexpr double kWaitFloorUs = 50.0;
 // Blocks per lane in team launches: kTeamKR in VGPRs plus kTeamKL in LDS.  20 per lane with
 // two workgroups per CU measured best on the 64-expert MoE batch (24: no gain over two passes,
 // 16: slower).  18 + 2 leaves the registers that the loop over tensors needs without spilling
@@ -814,6 +822,7 @@ __device__ __noinline__ uint32_t wg_tensor_amax(const uint4* __restrict__ p, int
   __syncthreads();
   uint32_t r = part[0];
   for (int w = 1; w < kThreads / 64; ++w) r = max(r, part[w]);
+  __syncthreads();   // every wave has read part[] before any reuses it (the next tensor)
   return r;
 }
 
@@ -866,7 +875,8 @@ template <int MODE, int RULE, bool FQ, int KR, int KL>
 __device__ __forceinline__ void fused_tensor(
     int64_t t, uint32_t tid, const uint4* __restrict__ in, int64_t nblk,
     uint32_t* __restrict__ ws, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-    uint4* __restrict__ out, float* __restrict__ alpha_out, uint32_t wait_limit, BlockTables& tb,
+    uint4* __restrict__ out, float* __restrict__ alpha_out, uint32_t wait_polls,
+    uint64_t wait_ticks, BlockTables& tb,
     uint4 (&held)[KL > 0 ? KL : 1][2][kThreads], uint32_t* part, uint32_t& amax_sh) {
   const uint32_t G = gridDim.x, g = blockIdx.x;
   const uint32_t n = (uint32_t)nblk;
@@ -948,9 +958,10 @@ __device__ __forceinline__ void fused_tensor(
       }
     }
     uint32_t polls = 0, flag;
+    const uint64_t t0 = wall_clock64();
     while (!((flag = __hip_atomic_load(line + 2, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT)) & 1u)) {
-      if (polls++ >= wait_limit) break;
+      if (polls++ >= wait_polls || wall_clock64() - t0 > wait_ticks) break;
       __builtin_amdgcn_s_sleep(2);
     }
     amax_sh = (flag & 1u) ? (flag & ~1u) : 0xFFFFFFFFu;   // 0xFFFFFFFF: "compute it here"
@@ -975,7 +986,7 @@ __device__ __forceinline__ void fused_tensor(
   }
   build_tables<MODE>(tb, alpha);
   __syncthreads();
-  const bool tiny_alpha = alpha < 3.3306691e-36f;   // 2^-118: 1/d may overflow
+  const bool tiny_alpha = alpha < 0x1p-118f;   // 1/d may overflow below 2^-118
   // Phase 2 is bound by the VALU and every workgroup starts it at once: the waves pace
   // themselves as in quantize_kernel (issue priority 3, 2, 1, 0 by quarters of the held blocks).
   constexpr int K = KR + KL;
@@ -1013,14 +1024,15 @@ template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fused_kernel(
     const uint4* __restrict__ in, int64_t nblk, uint32_t* __restrict__ ws,
     uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
-    float* __restrict__ alpha_out, uint32_t wait_limit, int64_t E) {
+    float* __restrict__ alpha_out, uint32_t wait_polls, uint64_t wait_ticks, int64_t E) {
   __shared__ BlockTables tb;
   __shared__ uint4 held[KL > 0 ? KL : 1][2][kThreads];
   __shared__ uint32_t part[kThreads / 64];
   __shared__ uint32_t amax_sh;
   if (!TEAMS) {
     fused_tensor<MODE, RULE, FQ, KR, KL>(blockIdx.y, threadIdx.x, in, nblk, ws, codes, scales, out,
-                                         alpha_out, wait_limit, tb, held, part, amax_sh);
+                                         alpha_out, wait_polls, wait_ticks, tb, held, part,
+                                         amax_sh);
     return;
   }
   // Teams that start together stay in step: all load, then all compute, and memory idles while
@@ -1030,7 +1042,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // up only costs the overlap.  Measured on the 64-expert MoE batch: 445 against 495 us.
   if ((blockIdx.y & 1) && threadIdx.x == 0) {
     const uint32_t* flag = ws + (blockIdx.y - 1) * kFusedWsWords + 2;
-    for (uint32_t polls = 0; polls < wait_limit &&
+    const uint64_t t0 = wall_clock64();
+    for (uint32_t polls = 0; polls < wait_polls && wall_clock64() - t0 <= wait_ticks &&
          !(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u); ++polls)
       __builtin_amdgcn_s_sleep(2);
   }
@@ -1041,7 +1054,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     uint32_t tid;
     asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(threadIdx.x));
     fused_tensor<MODE, RULE, FQ, KR, KL>(t, tid, in, nblk, ws, codes, scales, out, alpha_out,
-                                         wait_limit, tb, held, part, amax_sh);
+                                         wait_polls, wait_ticks, tb, held, part, amax_sh);
   }
 }
 
@@ -1324,7 +1337,29 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
 }
 
 // ----------------------------------------------------------------------------- fused (host)
-std::atomic<uint32_t> g_wait_limit{kFusedDefaultWaitLimit};
+std::atomic<uint32_t> g_wait_polls{kFusedMaxWaitPolls};
+
+// Ticks per microsecond of the device's constant-rate wall clock (the clock the waits read),
+// cached per device; 100 (100 MHz) if the attribute is unavailable.
+double wall_ticks_per_us() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100.0;
+  int khz = cache[dev].load(std::memory_order_relaxed);
+  if (khz == 0) {
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        khz <= 0)
+      khz = 100000;
+    cache[dev].store(khz, std::memory_order_relaxed);
+  }
+  return khz / 1000.0;
+}
+
+// Time bound of the waits of a fused launch in which `at_once` tensors are loaded together.
+uint64_t fused_wait_ticks(const Shape& s, int64_t at_once) {
+  const double us = kWaitFactor * (double)at_once * (double)s.n * 2.0 / kWaitLoadRate + kWaitFloorUs;
+  return (uint64_t)(us * wall_ticks_per_us());
+}
 
 // Workgroups of one fused_kernel instance that fit on the current device at once (occupancy
 // per CU times the CU count), cached per device; 0 if unknown.
@@ -1386,7 +1421,8 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
   hipLaunchKernelGGL((fused_kernel<MODE, RULE, FQ, KR, KL, TEAMS>), dim3((unsigned)G, (unsigned)T),
                      dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(in), s.nblk, ws,
                      reinterpret_cast<uint2*>(codes), scales, reinterpret_cast<uint4*>(out), alpha,
-                     g_wait_limit.load(std::memory_order_relaxed), s.E);
+                     g_wait_polls.load(std::memory_order_relaxed), fused_wait_ticks(s, T),
+                     s.E);
 }
 
 // Tiers of blocks held per lane: (KR in VGPRs, KL in LDS) = (1,0), (4,0), (12,0), (20,8).  The
@@ -1622,7 +1658,7 @@ NVFP4_EXPORT int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols,
 }
 
 NVFP4_EXPORT void nvfp4_fused_set_wait_limit(int64_t polls) {
-  g_wait_limit.store(polls < 0 ? kFusedDefaultWaitLimit
-                               : (uint32_t)std::min<int64_t>(polls, kFusedMaxWaitLimit),
+  g_wait_polls.store(polls < 0 ? kFusedMaxWaitPolls
+                               : (uint32_t)std::min<int64_t>(polls, kFusedMaxWaitPolls),
                      std::memory_order_relaxed);
 }
