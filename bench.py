@@ -1,21 +1,27 @@
 """Benchmark: NVFP4 Four Over Six quantization on one MI355X.
 
-One step is one pass of the whole hot path over one synthetic tensor: the amax
+One step is one pass of the whole hot path over one synthetic input: the amax
 pass (clear + streaming max), then the block pass (alpha, both candidate scales,
 FP4 rounding, error, selection, packed codes + E4M3 scales).  The step calls the
 C-ABI entry points nvfp4_amax and nvfp4_quantize_from_amax back to back -- the
-kernels of nvfp4_quantize, in the same order.
+kernels of nvfp4_quantize_batched, in the same order.
 
-Default workload: the 4096 x 14336 bf16 weight (N(0, 0.02^2), 0.1 % of entries
-x20), Four Over Six with the MSE rule, packed output.  Inputs are generated once
-on the host, copied to HBM and rotated over enough copies that each step starts
-on data the 256 MB Infinity Cache no longer holds.
+Default workload: the largest configuration, a mixture-of-experts weight batch of
+64 experts of 2048 x 5120 bf16 (expert e: sigma_e * N(0, 1), sigma_e
+log-uniform in [0.005, 0.05]), Four Over Six with the MSE rule, packed output,
+one alpha per expert, one launch per pass.  `--workload weight|act|large|tiny`
+selects the other configurations.  Inputs are generated once on the host,
+copied to HBM and rotated over enough copies that each step starts on data the
+256 MB Infinity Cache no longer holds.
 
 Timing:
   * timed region: K steps captured as one HIP graph and replayed once, bracketed
     by torch.cuda.synchronize() (so host launch overhead is not timed); gives
-    ms_per_step and value = algorithmic bytes per step / step time
-    (2 B/elem amax read + 2.5625 B/elem block pass, or 4 B/elem fake-quant).
+    ms_per_step and value = the operation's own bytes / step time: the bf16
+    input once plus the codes and scales out (2.5625 B/elem), or the bf16 input
+    and output (4 B/elem fake-quant).  The HBM bytes the two-pass step moves
+    (the amax pass reads the input a second time: 4.5625 or 6 B/elem) are
+    reported separately as hbm_bytes_per_step.
   * per-kernel legs: graphs of back-to-back launches of one pass over rotating
     cold buffers, HIP events recorded on the launch stream before and after the
     replay; the average launch of the block pass is the roofline figure.  Also
@@ -101,7 +107,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="weight")
+    ap.add_argument("--workload", default="moe")
     ap.add_argument("--mode", default="four_over_six")
     ap.add_argument("--rule", default="mse")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -242,7 +248,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / K
-    value = step_bpe * N / (ms_step * 1e-3) / 1e9
+    value = pass_bpe * N / (ms_step * 1e-3) / 1e9          # the operation's own bytes
     del g_warm, g_steps
     log("[bench] timed region: %.1f us/step" % (ms_step * 1e3))
 
@@ -307,7 +313,10 @@ def main():
             "amax": {"avg_us": round(legs["amax"], 2),
                      "GBps": round(AMAX_BPE * N / (legs["amax"] * 1e-6) / 1e9, 1),
                      "replay_min_max_us": spread["amax"]},
-            "step": {"Gelem_per_s": round(N / (ms_step * 1e-3) / 1e9, 2)},
+            "step": {"Gelem_per_s": round(N / (ms_step * 1e-3) / 1e9, 2),
+                     "op_bytes_per_step": int(pass_bpe * N),
+                     "hbm_bytes_per_step": int(step_bpe * N),
+                     "hbm_GBps": round(step_bpe * N / (ms_step * 1e-3) / 1e9, 1)},
             "dynamic_entry_point": {"avg_us": round(legs["dynamic_entry_point"], 2)},
             "fused_entry_point": {
                 "avg_us": round(legs["fused_entry_point"], 2),
@@ -349,20 +358,33 @@ def main():
         del src, dst
 
     if not args.no_cpu_baseline and not args.profile:
-        result["cpu_baseline"] = cpu_baseline(x_cpu, wl, args, step_bpe)
+        result["cpu_baseline"] = cpu_baseline(x_cpu, wl, args, pass_bpe)
 
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(x_cpu, wl, args, step_bpe):
+def cpu_threads():
+    """(threads used, CPUs this process may run on, CPUs the host reports).  The oracle runs
+    on every CPU it may use, up to 16: a one-GPU machine allots 16 host CPUs to its GPU, whatever
+    the host reports."""
+    host = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = host
+    return max(1, min(16, usable)), usable, host
+
+
+def cpu_baseline(x_cpu, wl, args, bpe):
     """The CPU oracle (untuned, test infrastructure) on a bounded sample of the workload:
     the whole hot path (amax + block pass) on the leading rows of the tensor (the first
-    experts for batched workloads), on the host's cores; median of repeated runs."""
+    experts for batched workloads), on the host's cores; median of repeated runs.  GB/s on
+    the same bytes as the GPU value (the operation's own bytes)."""
     import numpy as np
 
     import oracle
     from nvfp4_block_scaled_amax_amd import workloads as W
-    cores = max(1, min(16, os.cpu_count() or 1))
+    cores, usable, host = cpu_threads()
     x = W.bits(x_cpu)
     if x.ndim == 3:
         sample = x[:2]
@@ -387,10 +409,13 @@ def cpu_baseline(x_cpu, wl, args, step_bpe):
         oracle.quantize(small, args.mode, args.rule, nthreads=1, want_y=False)
         t1.append(time.perf_counter() - t0)
     dt1 = float(np.median(t1))
-    return {"value": round(step_bpe * sample.size / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+    return {"value": round(bpe * sample.size / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle", "sample": desc + ", median of %d runs" % reps,
             "seconds_per_run": round(dt, 3), "cpu_model": cpu_model(),
-            "single_thread": {"value": round(step_bpe * small.size / dt1 / 1e9, 4),
+            "host_cpus": host, "usable_cpus": usable,
+            "threads_note": "the oracle's threads: every usable CPU up to 16, the host CPUs "
+                            "a one-GPU box allots to its GPU",
+            "single_thread": {"value": round(bpe * small.size / dt1 / 1e9, 4),
                               "unit": "GB/s", "cores": 1,
                               "sample": "first %d elements of that sample, median of 3 runs"
                                         % small.size,
