@@ -8,13 +8,28 @@ The arithmetic lives in ``nvfp4_oracle.cpp`` (plain C++17, brute-force rounding,
 binary32 steps in the order the pages describe).  This module builds it with g++
 and wraps it with ctypes over numpy arrays.
 
-Pinned functions (see tests/test_oracle_pins.py): E2M1 decode/round, E4M3
-encode/decode, bf16 rounding, alpha, block quantization (both modes, three
-rules), whole-tensor and sampled-block quantization.  Nothing here is
-"parity unpinned".
+What pins each function (tests/test_oracle_pins.py, tests/test_oracle_shadow.py,
+tests/test_oracle_mutants.py):
+  e2m1_*, e4m3_*, bf16_rne   the printed FP4 value set, an independent threshold
+                             formulation, torch's float8_e4m3fn and bfloat16 casts
+  alpha                      closed forms and exact rationals
+  quantize_block, candidate, worked examples derived by hand, exact-rational brute
+  quantize                   force, the pages' 66.6 % and 75 % facts, invariants
+  amax                       an independent numpy max over batches with NaN, +-Inf,
+                             -0 and subnormals
+  quantize_blocks            equal to quantize on every block id and on shuffled
+                             subsets of batches with a different alpha per tensor
+  dequantize                 closed forms; equal to the fake-quant output
+  quantize_stats             hand-derived statistics and exact-rational sums
+  shadow_block,              exact-rational brute force of the exact-quotient
+  shadow_compare             reading, closed forms, and equality with the binary32
+                             reading where no rounding intervenes
+The planted-mistake tests build mutated copies of the C++ source and check that
+the pins above reject each of them.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -48,13 +63,38 @@ class _BlockDebug(ctypes.Structure):
                 ("err6", ctypes.c_float), ("err4", ctypes.c_float)]
 
 
+class _ShadowCounts(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "blocks", "scale_diff", "choice_diff", "block_diff", "code_diff", "y_diff",
+        "exact_ties", "inexact")]
+
+
 _lib = None
 
 
 def lib():
     global _lib
     if _lib is None:
-        L = ctypes.CDLL(build())
+        _lib = _bind(build())
+    return _lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Route every function of this module to another build of the oracle for the duration
+    (the planted-mistake tests load mutated copies of the source this way)."""
+    global _lib
+    saved = _lib
+    _lib = _bind(path)
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    if True:
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i64, i32, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_float
         L.orc_e2m1_decode.argtypes, L.orc_e2m1_decode.restype = [i32], f32
@@ -78,8 +118,12 @@ def lib():
         L.orc_quantize_stats.argtypes = [P, i64, i64, i64, i32, i32, P, i32]
         L.orc_quantize_stats.restype = i32
         L.orc_inexact_subtractions.restype = i64
-        _lib = L
-    return _lib
+        L.orc_shadow_block.argtypes = [P, f32, i32, i32, i32, P, P, P, P]
+        L.orc_shadow_compare.argtypes = [P, i64, i64, i64, i32, i32, i32,
+                                         ctypes.POINTER(_ShadowCounts), i32]
+        L.orc_shadow_compare.restype = i32
+        L.orc_shadow_inexact.restype = i64
+    return L
 
 
 def _p(a: np.ndarray):
@@ -243,3 +287,40 @@ def quantize_stats(x_bits: np.ndarray, mode="four_over_six", rule="mse",
 
 def inexact_subtractions() -> int:
     return int(lib().orc_inexact_subtractions())
+
+
+# ---- exact-quotient shadow (a diagnostic reading, not the parity target) -------------
+def shadow_block(x16_bits, a, mode, rule, exact_alpha: bool = False):
+    """One block under the exact-quotient reading: (codes[8] u8, scale u8, y[16] u16, qstar).
+    a is the binary32 alpha, or with exact_alpha the tensor amax (alpha = amax / (6*M)
+    exactly)."""
+    x = np.ascontiguousarray(x16_bits, dtype=np.uint16)
+    assert x.size == 16
+    codes = np.zeros(8, np.uint8)
+    scale = np.zeros(1, np.uint8)
+    y = np.zeros(16, np.uint16)
+    q = ctypes.c_int(0)
+    lib().orc_shadow_block(_p(x), float(a), _mode(mode), _rule(rule), int(bool(exact_alpha)),
+                           _p(codes), _p(scale), _p(y), ctypes.byref(q))
+    return codes, int(scale[0]), y, q.value
+
+
+def shadow_compare(x_bits: np.ndarray, mode="four_over_six", rule="mse",
+                   exact_alpha: bool = False, nthreads: int = 1) -> dict:
+    """Counts of what differs between the binary32 reading and the exact-quotient reading
+    (after the binary32 alpha, or with exact_alpha fully exact) over whole tensors
+    ([rows, cols] or [E, rows, cols])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    E = x.shape[0] if x.ndim == 3 else 1
+    rows, cols = x.shape[-2], x.shape[-1]
+    c = _ShadowCounts()
+    rc = lib().orc_shadow_compare(_p(x), E, rows, cols, _mode(mode), _rule(rule),
+                                  int(bool(exact_alpha)), ctypes.byref(c), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected arguments (rc=%d)" % rc)
+    return {name: int(getattr(c, name)) for name, _ in _ShadowCounts._fields_}
+
+
+def shadow_inexact() -> int:
+    """Failed exactness checks of the shadow's own arithmetic in shadow_block calls (0)."""
+    return int(lib().orc_shadow_inexact())

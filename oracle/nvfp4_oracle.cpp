@@ -18,6 +18,7 @@
 namespace {
 
 std::atomic<int64_t> g_inexact{0};
+std::atomic<int64_t> g_shadow_inexact{0};   // the exact shadow's own checks (expected 0)
 
 float f32_from_bits(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
 uint32_t bits_from_f32(float f) { uint32_t u; std::memcpy(&u, &f, 4); return u; }
@@ -255,6 +256,193 @@ void parallel_ranges(int64_t n, int nthreads, F&& fn) {
   for (auto& t : ts) t.join();
 }
 
+// ----------------------------------------------------------------------------- exact shadow
+// The exact-quotient reading of the same encoding: no step rounds except the encodings
+// themselves (E4M3 scale, E2M1 codes, bf16 output), either after the binary32 per-tensor scale
+// alpha (an FP32 value of the format) or with alpha = amax / (6*M) taken exactly.  Values live
+// in x87 extended precision (64-bit significand):
+//   Q*alpha                 2 + 24 significant bits   exact
+//   dec(s) * alpha          4 + 24                    exact
+//   t * dec(s) * Q * alpha  products of the grids' values (at most 2 bits each) with the above,
+//                           at most 32 bits           exact
+// (with alpha exact, every value is scaled by 6*M, at most 5 significant bits, and alpha
+// becomes the 8-bit amax: fewer bits still)
+// so every product below is exact, and every distance that can decide a nearest value or a
+// tie (a difference of a bf16 value, 8 bits, and such a product of similar magnitude) is exact
+// too.  The error terms e = x - xhat are checked for exactness with an error-free sum, and the
+// error sums are taken exactly in a fixed-point integer, so the choice between 6 and 4 is the
+// one exact arithmetic makes.
+typedef long double xf;
+
+// Exact sum of non-negative terms m * 2^k (m < 2^128): a 768-bit fixed-point integer whose
+// least bit weighs 2^-kExactLo.  e is a multiple of 2^-159 (bf16 inputs are multiples of
+// 2^-133, and val * dec(s) * alpha of 2^-1 * 2^-9 * 2^-149) and below 2^130, so e^2 and |e|
+// and sums of 16 of them fit with room to spare.
+constexpr int kExactLo = 330;
+constexpr int kExactLimbs = 12;
+struct ExactSum {
+  uint64_t w[kExactLimbs] = {};
+  bool out_of_range = false;
+  void add64(uint64_t v, int p) {
+    int i = p / 64;
+    const int sh = p % 64;
+    uint64_t lo = v << sh, hi = sh ? v >> (64 - sh) : 0;
+    for (; i < kExactLimbs && (lo | hi); ++i) {
+      const uint64_t old = w[i];
+      w[i] += lo;
+      const uint64_t carry = w[i] < old ? 1 : 0;
+      lo = hi + carry;
+      hi = (lo < carry) ? 1 : 0;        // hi + carry wrapped only if hi was all ones
+    }
+    if (lo | hi) out_of_range = true;
+  }
+  void add(unsigned __int128 m, int k) {
+    const int p = k + kExactLo;
+    if (p < 0 || p + 128 > 64 * kExactLimbs) { out_of_range = true; return; }
+    add64(uint64_t(m), p);
+    add64(uint64_t(m >> 64), p + 64);
+  }
+};
+
+int exact_cmp(const ExactSum& a, const ExactSum& b) {
+  for (int i = kExactLimbs - 1; i >= 0; --i)
+    if (a.w[i] != b.w[i]) return a.w[i] < b.w[i] ? -1 : 1;
+  return 0;
+}
+
+// |v| = m * 2^k with m odd (v != 0 and exact in xf).
+void split_exact(xf v, uint64_t* m, int* k) {
+  int e = 0;
+  const xf f = std::frexp(std::fabs(v), &e);     // [0.5, 1)
+  uint64_t mm = uint64_t(std::ldexp(f, 64));      // 64-bit significand, an integer
+  int kk = e - 64;
+  while ((mm & 1) == 0) { mm >>= 1; ++kk; }
+  *m = mm;
+  *k = kk;
+}
+
+// Nearest E4M3 byte to sigma = bmax / qa (qa = Q*alpha > 0) by exact distance, ties to the
+// even byte: |bmax - dec(b)*qa| = |sigma - dec(b)| * qa.  Above 448 the nearest is 448 itself,
+// which is the saturation of the binary32 reading too.
+int exact_e4m3(xf bmax, xf qa) {
+  int best = 0;
+  xf bestd = bmax;
+  for (int b = 1; b <= 0x7E; ++b) {
+    const xf dist = std::fabs(bmax - xf(e4m3_value(b)) * qa);
+    if (dist < bestd || (dist == bestd && (b & 1) == 0)) { best = b; bestd = dist; }
+  }
+  return best;
+}
+
+// Nearest E2M1 magnitude code to a / D (D > 0) by exact distance, ties to the even code;
+// above 6 the nearest is 6 (saturation).
+int exact_e2m1(xf a, xf D) {
+  int best = 0;
+  xf bestd = a;
+  for (int c = 1; c < 8; ++c) {
+    const xf dist = std::fabs(a - xf(kE2M1Mag[c]) * D);
+    if (dist < bestd || (dist == bestd && (c & 1) == 0)) { best = c; bestd = dist; }
+  }
+  return best;
+}
+
+// Nearest bfloat16 to v / c for an exact v and c in {1, 1536, 2688} (ties to the even
+// pattern): the nearest lies next to the truncation of the quotient's binary32 rounding, and
+// |v - c * value(p)| compares the candidates exactly (c * value(p) has at most 13 bits).
+uint16_t bf16_rne_exact(xf v, xf c) {
+  const bool neg = std::signbit(v);
+  const xf a = std::fabs(v);
+  const uint16_t t = uint16_t(bits_from_f32(float(a / c)) >> 16);
+  uint16_t best = t;
+  xf bestd = std::fabs(a - c * xf(bf16_pattern_value(t)));
+  for (int dlt = -1; dlt <= 1; dlt += 2) {
+    const int p = int(t) + dlt;
+    if (p < 0 || p > 0x7F80) continue;
+    const xf dist = std::fabs(a - c * xf(bf16_pattern_value(uint16_t(p))));
+    if (dist < bestd || (dist == bestd && (p & 1) == 0)) { best = uint16_t(p); bestd = dist; }
+  }
+  return uint16_t(best | (neg ? 0x8000 : 0));
+}
+
+struct ExactCand {
+  int scale = 0;
+  uint8_t mag[16] = {};
+  xf xhat[16] = {};
+  ExactSum sum;          // MSE: sum of e^2; MAE: sum of |e|
+  xf maxerr = 0;         // MAXERR: max |e|
+};
+
+// One candidate target block maximum Q under exact arithmetic.  Every value is given scaled
+// by a common factor c (x[i] = c * x_i, bmax = c * bmax, a = c * alpha): with c = 1 and a the
+// binary32 alpha this is the exact reading after alpha; with c = 6*M and a = amax it is the
+// fully exact reading with alpha = amax / (6*M) as a rational.  The scale byte, the codes and
+// the choice do not depend on c (every comparison scales with it), and xhat and e come out
+// scaled by c.
+void exact_candidate(const xf x[16], xf bmax, xf a, int Q, int rule, ExactCand* c,
+                     int64_t* inexact) {
+  const xf qa = xf(Q) * a;
+  c->scale = a == 0 ? 0 : exact_e4m3(bmax, qa);
+  const xf D = xf(e4m3_value(c->scale)) * a;
+  const int cap = Q == 4 ? 6 : 7;                 // a block scaled to 4 stays within [-4, 4]
+  for (int i = 0; i < 16; ++i) {
+    const xf xi = x[i];
+    const int m = D == 0 ? 0 : std::min(exact_e2m1(std::fabs(xi), D), cap);
+    c->mag[i] = uint8_t(m);
+    const xf mag_hat = xf(kE2M1Mag[m]) * D;
+    c->xhat[i] = std::signbit(xi) ? -mag_hat : mag_hat;
+    // e = x - xhat, with Knuth's two-sum error term to confirm the subtraction is exact
+    const xf b = -c->xhat[i];
+    const xf e = xi + b;
+    const xf bb = e - xi;
+    const xf err = (xi - (e - bb)) + (b - bb);
+    if (err != 0) ++*inexact;
+    if (e == 0) continue;
+    if (rule == ORC_MAXERR) {
+      c->maxerr = std::max(c->maxerr, std::fabs(e));
+    } else {
+      uint64_t mm;
+      int kk;
+      split_exact(e, &mm, &kk);
+      if (rule == ORC_MSE) c->sum.add((unsigned __int128)mm * mm, 2 * kk);
+      else                 c->sum.add(mm, kk);
+    }
+  }
+  if (c->sum.out_of_range) ++*inexact;
+}
+
+// One block under the exact reading.  exact_alpha = false: a is the binary32 alpha;
+// exact_alpha = true: a is the tensor amax and alpha = amax / (6*M) exactly.
+void exact_block(const float xin[16], float a, int mode, int rule, bool exact_alpha,
+                 uint8_t codes8[8], uint8_t* scale, uint16_t y16[16], int* qstar, bool* tie,
+                 int64_t* inexact) {
+  const xf c = exact_alpha ? xf(mode == ORC_FOUR_OVER_SIX ? 1536 : 2688) : xf(1);
+  xf x[16];
+  xf bmax = 0;
+  for (int i = 0; i < 16; ++i) {
+    x[i] = c * xf(xin[i]);                        // exact: 8 + 5 significant bits
+    bmax = std::max(bmax, std::fabs(x[i]));
+  }
+  ExactCand c6, c4;
+  exact_candidate(x, bmax, xf(a), 6, rule, &c6, inexact);
+  const ExactCand* win = &c6;
+  *tie = false;
+  if (mode == ORC_FOUR_OVER_SIX) {
+    exact_candidate(x, bmax, xf(a), 4, rule, &c4, inexact);
+    const int cmp = rule == ORC_MAXERR ? (c4.maxerr < c6.maxerr ? -1 : c4.maxerr > c6.maxerr ? 1 : 0)
+                                       : exact_cmp(c4.sum, c6.sum);
+    if (cmp < 0) win = &c4;                       // a tie keeps 6
+    *tie = cmp == 0;
+  }
+  *scale = uint8_t(win->scale);
+  for (int j = 0; j < 8; ++j) {
+    const int lo = (std::signbit(xin[2 * j]) ? 8 : 0) | win->mag[2 * j];
+    const int hi = (std::signbit(xin[2 * j + 1]) ? 8 : 0) | win->mag[2 * j + 1];
+    codes8[j] = uint8_t(lo | (hi << 4));
+  }
+  if (y16) for (int i = 0; i < 16; ++i) y16[i] = bf16_rne_exact(win->xhat[i], c);
+  *qstar = win == &c4 ? 4 : 6;
+}
+
 bool bad_args(const void* in, int64_t E, int64_t rows, int64_t cols, int mode, int rule) {
   return !in || E <= 0 || rows <= 0 || cols <= 0 || cols % 16 != 0 ||
          (mode != ORC_RTN6 && mode != ORC_FOUR_OVER_SIX) ||
@@ -434,5 +622,72 @@ int orc_quantize_stats(const uint16_t* in, int64_t E, int64_t rows, int64_t cols
 }
 
 int64_t orc_inexact_subtractions(void) { return g_inexact.load(); }
+
+void orc_shadow_block(const uint16_t* x16, float a, int mode, int rule, int exact_alpha,
+                      uint8_t* codes8, uint8_t* scale, uint16_t* y16, int* qstar) {
+  float x[16];
+  for (int i = 0; i < 16; ++i) x[i] = bf16_value(x16[i]);
+  bool tie = false;
+  int64_t inexact = 0;
+  exact_block(x, a, mode, rule, exact_alpha != 0, codes8, scale, y16, qstar, &tie, &inexact);
+  g_shadow_inexact.fetch_add(inexact);
+}
+
+int64_t orc_shadow_inexact(void) { return g_shadow_inexact.load(); }
+
+int orc_shadow_compare(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int mode,
+                       int rule, int exact_alpha, orc_shadow_counts* out, int nthreads) {
+  if (bad_args(in, E, rows, cols, mode, rule) || !out) return -1;
+  const int64_t n = rows * cols, nb = n / 16;
+  const int nt = std::max(1, nthreads);
+  std::vector<orc_shadow_counts> parts(nt);
+  for (auto& p : parts) std::memset(&p, 0, sizeof p);
+  for (int64_t t = 0; t < E; ++t) {
+    const uint16_t* x = in + t * n;
+    const float amax = tensor_amax(x, n);
+    if (std::isnan(amax)) continue;               // poisoned tensor: nothing to compare
+    const float al = alpha_of(amax, mode);
+    const int64_t chunk = (nb + nt - 1) / nt;
+    parallel_ranges(nb, nt, [&](int64_t lo, int64_t hi) {
+      orc_shadow_counts& c = parts[lo / std::max<int64_t>(1, chunk)];
+      for (int64_t b = lo; b < hi; ++b) {
+        float xb[16];
+        for (int i = 0; i < 16; ++i) xb[i] = bf16_value(x[b * 16 + i]);
+        uint8_t c32[8], cx[8], s32, sx;
+        uint16_t y32[16], yx[16];
+        orc_block_debug dbg;
+        quantize_block(xb, al, mode, rule, c32, &s32, y32, &dbg);
+        int qx = 0;
+        bool tie = false;
+        exact_block(xb, exact_alpha ? amax : al, mode, rule, exact_alpha != 0, cx, &sx, yx, &qx,
+                    &tie, &c.inexact);
+        ++c.blocks;
+        int dc = 0, dy = 0;
+        for (int i = 0; i < 16; ++i) {
+          dc += ((c32[i / 2] >> (4 * (i & 1))) & 0xF) != ((cx[i / 2] >> (4 * (i & 1))) & 0xF);
+          dy += y32[i] != yx[i];
+        }
+        c.code_diff += dc;
+        c.y_diff += dy;
+        c.scale_diff += s32 != sx;
+        c.choice_diff += dbg.qstar != qx;
+        c.block_diff += (dc > 0 || s32 != sx);
+        c.exact_ties += tie;
+      }
+    });
+  }
+  std::memset(out, 0, sizeof *out);
+  for (const auto& p : parts) {
+    out->blocks += p.blocks;
+    out->scale_diff += p.scale_diff;
+    out->choice_diff += p.choice_diff;
+    out->block_diff += p.block_diff;
+    out->code_diff += p.code_diff;
+    out->y_diff += p.y_diff;
+    out->exact_ties += p.exact_ties;
+    out->inexact += p.inexact;
+  }
+  return 0;
+}
 
 }  // extern "C"

@@ -99,6 +99,37 @@ int      orc_quantize_stats(const uint16_t* in, int64_t E, int64_t rows, int64_t
 /* Count of error subtractions e = x - xhat that were not exact (expected 0). */
 int64_t  orc_inexact_subtractions(void);
 
+/* Exact-quotient shadow: the same encoding read with exact arithmetic after the per-tensor
+ * scale.  Per block and candidate Q: sigma = bmax / (Q*alpha) exactly, s = E4M3 RNE of sigma
+ * (saturating at 448), D = dec(s) * alpha exactly, code = E2M1 RNE of |x| / D exactly (capped
+ * at 4 for Q = 4), xhat = val(code) * D exactly, e = x - xhat exactly, and the error sums or
+ * max exactly; the smaller error wins, ties keep 6 [4/6, "Adaptive block scaling algorithm":
+ * both errors against the original high-precision values].  Fake-quant: y = RNbf16(xhat).
+ * exact_alpha = 0: `a` is the binary32 alpha (an FP32 value of the format);
+ * exact_alpha = 1: `a` is the tensor amax and alpha = amax / (6*M) is taken exactly.
+ * A diagnostic of how far the binary32 reading departs from exact arithmetic; not what the
+ * GPU path is checked against. */
+void     orc_shadow_block(const uint16_t* x16, float a, int mode, int rule, int exact_alpha,
+                          uint8_t* codes8, uint8_t* scale, uint16_t* y16, int* qstar);
+/* Count of the shadow's exactness checks (error subtractions, exact sums) that failed in
+ * orc_shadow_block calls so far (expected 0). */
+int64_t  orc_shadow_inexact(void);
+
+/* Both readings over whole tensors ([E][rows][cols], alpha per tensor from the tensor amax as
+ * in orc_quantize; poisoned tensors are skipped), with counts of what differs. */
+typedef struct {
+  int64_t blocks;        /* blocks compared */
+  int64_t scale_diff;    /* blocks whose chosen scale byte differs */
+  int64_t choice_diff;   /* blocks whose choice between 6 and 4 differs */
+  int64_t block_diff;    /* blocks with any code or scale byte that differs */
+  int64_t code_diff;     /* 4-bit element codes that differ */
+  int64_t y_diff;        /* fake-quant bf16 values that differ */
+  int64_t exact_ties;    /* Four Over Six blocks whose two exact errors are equal */
+  int64_t inexact;       /* exactness checks of the shadow's own arithmetic that failed (0) */
+} orc_shadow_counts;
+int      orc_shadow_compare(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int mode,
+                            int rule, int exact_alpha, orc_shadow_counts* out, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -598,3 +598,81 @@ def test_stats_poisoned_tensor_is_nan(orc):
     x[1, 3, 7] = 0x7F80                               # +inf
     st = orc.quantize_stats(x, "four_over_six", "mse")
     assert np.isnan(st[1]).all() and np.isfinite(st[[0, 2]]).all()
+
+
+# ----------------------------------------------------------------------------- amax, sampled blocks
+def _amax_by_numpy(x_bits: np.ndarray, E: int) -> np.ndarray:
+    """Per-tensor max |x| of E equal tensors computed with numpy from the bf16 bit patterns
+    (bf16 -> binary32 is a 16-bit shift); NaN for a tensor holding a NaN or an infinity."""
+    v = bf16_to_f32(np.asarray(x_bits, np.uint16).reshape(E, -1))
+    out = np.abs(v).max(axis=1).astype(np.float32)
+    out[~np.isfinite(v).all(axis=1)] = np.nan
+    return out
+
+
+def test_amax_of_batches_with_special_values(orc):
+    """The per-tensor amax alpha is computed from [4/6, "Implementation details"], pinned to
+    an independent numpy reduction: batches with -0, subnormals, +-Inf and NaN, tensors whose
+    max sits at their first or last element, and one-element tensors."""
+    rng = np.random.default_rng(41)
+    E, n = 7, 48
+    v = (rng.standard_normal((E, n)).astype(np.float32)
+         * np.float32(2.0) ** rng.integers(-20, 20, size=(E, 1)).astype(np.float32))
+    x = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    x[0] = 0x8000                                      # all -0: amax 0
+    x[1] = rng.integers(1, 0x80, size=n) | (rng.integers(0, 2, size=n) << 15)   # subnormals
+    x[2, -1] = 0xF149                                  # max at the last element, negative
+    x[3, 0] = 0x7A00                                   # max at the first element
+    x[4, 11] = 0xFF80                                  # -Inf
+    x[5, 30] = 0x7FC1                                  # NaN
+    x[6, 3] = 0x7F80                                   # +Inf
+    got = orc.amax(x, E)
+    want = _amax_by_numpy(x, E)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok].view(np.uint32), want[ok].view(np.uint32))
+    assert got[0] == 0.0 and not np.signbit(got[0])
+    # each tensor alone gives its own value: no tensor's amax leaks into another's
+    for e in range(E):
+        one = orc.amax(x[e], 1)
+        assert np.array_equal(np.isnan(one), np.isnan(want[e:e + 1]))
+        if ok[e]:
+            assert one[0] == want[e]
+    # one-element tensors (n = 1): the max is the magnitude of the element itself
+    single = np.array([0xC020, 0x3F40, 0x8000, 0x000B], np.uint16)   # -2.5, 0.75, -0, 2^-130*11
+    assert np.array_equal(orc.amax(single, 4), np.abs(bf16_to_f32(single)))
+
+
+def test_sampled_blocks_equal_the_whole_tensor_result(orc):
+    """orc.quantize_blocks (the checker of sampled blocks at full size) gives, for every block
+    id of a batch with one alpha per tensor (from orc.amax and orc.alpha), exactly what
+    orc.quantize gives for the whole batch, and the same on shuffled subsets of ids."""
+    x = _small("moe", (5, 24, 96))                     # 5 tensors, sigma from 0.005 to 0.05
+    E = x.shape[0]
+    for mode, rule in (("four_over_six", "mse"), ("four_over_six", "maxerr"), ("rtn6", "mse")):
+        whole = orc.quantize(x, mode, rule, want_qstar=True)
+        al = np.array([orc.alpha(a, mode) for a in orc.amax(x, E)], np.float32)
+        assert np.array_equal(al.view(np.uint32), whole["alpha"].view(np.uint32))
+        assert len(set(al.tolist())) == E              # every tensor has its own alpha
+        nb = x.size // 16
+        ids = np.arange(nb)
+        r = orc.quantize_blocks(x, al, ids, mode, rule)
+        assert np.array_equal(r["codes"], whole["codes"].reshape(-1, 8))
+        assert np.array_equal(r["scales"], whole["scales"].ravel())
+        assert np.array_equal(r["y"], whole["y"].reshape(-1, 16))
+        assert np.array_equal(r["qstar"], whole["qstar"].ravel())
+        rng = np.random.default_rng(42)
+        for k in (1, 17, nb // 3):
+            sel = rng.permutation(nb)[:k]
+            rs = orc.quantize_blocks(x, al, sel, mode, rule)
+            assert np.array_equal(rs["codes"], whole["codes"].reshape(-1, 8)[sel])
+            assert np.array_equal(rs["scales"], whole["scales"].ravel()[sel])
+            assert np.array_equal(rs["y"], whole["y"].reshape(-1, 16)[sel])
+    # a poisoned tensor (alpha NaN) poisons only its own sampled blocks
+    al = np.array([orc.alpha(a, "four_over_six") for a in orc.amax(x, E)], np.float32)
+    al[2] = np.nan
+    nb1 = x[0].size // 16
+    sel = np.array([2 * nb1 + 3, 1 * nb1 + 3, 3 * nb1 + 3])
+    rs = orc.quantize_blocks(x, al, sel, "four_over_six", "mse")
+    assert rs["scales"][0] == 0x7F and (rs["codes"][0] == 0).all()
+    assert rs["scales"][1] != 0x7F and rs["scales"][2] != 0x7F
