@@ -84,8 +84,9 @@ typedef enum {
   NVFP4_ERR_ENUM = 4,   /* mode or rule out of range */
   NVFP4_ERR_ALIGN = 5,  /* in/out/codes not 16-byte aligned, alpha/amax not 4-byte */
   NVFP4_ERR_HIP = 6,    /* a kernel launch failed */
-  NVFP4_ERR_ALIAS = 7   /* overlapping arguments (other than in-place fake-quant); added
+  NVFP4_ERR_ALIAS = 7,  /* overlapping arguments (other than in-place fake-quant); added
                            after the first six, so it takes the next free number */
+  NVFP4_ERR_SCRATCH = 8 /* nvfp4_quantize_fused_noalloc: E > NVFP4_NOALLOC_MAX_TENSORS */
 } nvfp4_status;
 
 /* ABI version (NVFP4_ABI_VERSION) and a static description of a status code. */
@@ -223,6 +224,23 @@ nvfp4_status nvfp4_quantize_fused(const uint16_t* in, int64_t E, int64_t rows, i
 nvfp4_status nvfp4_fakequant_fused(const uint16_t* in, int64_t E, int64_t rows, int64_t cols,
                                    int block, nvfp4_mode mode, nvfp4_rule rule, uint16_t* out,
                                    float* out_alpha, uint32_t* workspace, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): nvfp4_quantize_fused without the workspace
+ * argument.  The grid-wide wait's counters live in a static device array of the library
+ * (NVFP4_NOALLOC_MAX_TENSORS * NVFP4_FUSED_WS_WORDS words, 2.1 MiB, one copy per GPU, held
+ * until the process ends); the call allocates nothing, and at its first call on a device it
+ * looks up the array's address there.  Every call on one GPU shares that array, so calls that
+ * may overlap on one GPU (different streams, graph branches) race and must not be issued;
+ * calls in order on one stream are fine (each clears what it uses first).  Results, paths and
+ * errors as nvfp4_quantize_fused, plus NVFP4_ERR_SCRATCH for E > NVFP4_NOALLOC_MAX_TENSORS
+ * (returned before anything is enqueued). */
+#define NVFP4_NOALLOC_MAX_TENSORS 1024
+nvfp4_status nvfp4_quantize_fused_noalloc(const uint16_t* in, int64_t E, int64_t rows,
+                                          int64_t cols, int block, nvfp4_mode mode,
+                                          nvfp4_rule rule, uint8_t* out_codes,
+                                          uint8_t* out_scales, float* out_alpha,
+                                          hipStream_t stream);
 
 /* For a fused call of this shape, mode, rule and output form on the current device: the
  * most blocks a lane holds on chip (1, 4, 12 or 28; a tensor spread over more workgroups

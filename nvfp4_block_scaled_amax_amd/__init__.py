@@ -21,7 +21,8 @@ import torch
 
 __all__ = ["quantize", "fakequant", "amax", "quantize_from_amax", "fakequant_from_amax",
            "dequantize", "quantize_diag", "quantize_fused", "fakequant_fused",
-           "fused_blocks_per_lane", "set_fused_wait_limit", "diag_ws_words", "lib",
+           "quantize_fused_noalloc", "fused_blocks_per_lane", "set_fused_wait_limit",
+           "diag_ws_words", "lib",
            "NVFP4Error", "MODES", "RULES", "STATS", "FUSED_WS_WORDS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_amax.so")
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.nvfp4_quantize_diag.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.nvfp4_quantize_fused.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P, P]
         L.nvfp4_fakequant_fused.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
+        L.nvfp4_quantize_fused_noalloc.argtypes = [P, i64, i64, i64, i32, i32, i32, P, P, P, P]
         L.nvfp4_fused_single_read.argtypes = [i64, i64, i64, i32, i32, i32]
         L.nvfp4_fused_single_read.restype = i32
         L.nvfp4_fused_set_wait_limit.argtypes = [i64]
@@ -83,7 +85,8 @@ def lib() -> ctypes.CDLL:
         for name in ("nvfp4_amax", "nvfp4_quantize", "nvfp4_fakequant", "nvfp4_quantize_batched",
                      "nvfp4_fakequant_batched", "nvfp4_quantize_from_amax",
                      "nvfp4_fakequant_from_amax", "nvfp4_dequantize", "nvfp4_quantize_diag",
-                     "nvfp4_quantize_fused", "nvfp4_fakequant_fused"):
+                     "nvfp4_quantize_fused", "nvfp4_fakequant_fused",
+                     "nvfp4_quantize_fused_noalloc"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -290,6 +293,24 @@ def quantize_fused(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes=N
                                         _ptr(codes), _ptr(scales), _ptr(alpha), _ptr(ws),
                                         _stream(x))
     _check(st, "nvfp4_quantize_fused")
+    return codes, scales, alpha
+
+
+NOALLOC_MAX_TENSORS = 1024      # NVFP4_NOALLOC_MAX_TENSORS
+
+
+def quantize_fused_noalloc(x: torch.Tensor, mode="four_over_six", rule="mse", *, codes,
+                           scales, alpha):
+    """quantize_fused() whose wait counters live in the library's static device array: the
+    library allocates nothing (for callers that cannot allocate).  The outputs must be given.
+    Calls that may overlap on one GPU race on that array."""
+    E, rows, cols, batched = _dims(x)
+    codes, scales, alpha = _packed_outputs(x, E, rows, cols, batched, codes, scales, alpha)
+    with _on(x):
+        st = lib().nvfp4_quantize_fused_noalloc(_ptr(x), E, rows, cols, BLOCK, _mode(mode),
+                                                _rule(rule), _ptr(codes), _ptr(scales),
+                                                _ptr(alpha), _stream(x))
+    _check(st, "nvfp4_quantize_fused_noalloc")
     return codes, scales, alpha
 
 

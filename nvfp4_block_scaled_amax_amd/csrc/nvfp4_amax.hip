@@ -1502,6 +1502,38 @@ nvfp4_status run_fused(const uint16_t* in, int64_t E, int64_t rows, int64_t cols
 
 }  // namespace
 
+// ----------------------------------------------------------------------------- static scratch
+// The allocation-free single-read call keeps the grid-wide wait's counters here instead of
+// in a caller workspace: up to kScratchTensors tensors of NVFP4_FUSED_WS_WORDS words (2176
+// bytes each, 2.1 MiB in all).  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code the array's name is only a stand-in: its device address on a
+// device is taken once with hipGetSymbolAddress, with that device current, and that address
+// is what the kernels get.  Every call on a GPU shares the array, so calls that may overlap on
+// one GPU (different streams, graph branches) race; the launch clears what it uses first.
+constexpr int64_t kScratchTensors = NVFP4_NOALLOC_MAX_TENSORS;
+static __device__ __align__(256) uint32_t scratch[kScratchTensors * kFusedWsWords];
+
+namespace {
+
+std::atomic<uintptr_t> g_scratch_ptr[64];   // device address of `scratch` per device, 0 = not yet
+
+nvfp4_status scratch_on_current_device(uint32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return NVFP4_ERR_HIP;
+  uintptr_t p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == 0) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return NVFP4_ERR_HIP;
+    p = reinterpret_cast<uintptr_t>(ptr);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = reinterpret_cast<uint32_t*>(p);
+  return NVFP4_OK;
+}
+
+}  // namespace
+
 // ----------------------------------------------------------------------------- C ABI
 NVFP4_EXPORT int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
 
@@ -1515,6 +1547,8 @@ NVFP4_EXPORT const char* nvfp4_status_str(nvfp4_status st) {
     case NVFP4_ERR_ALIGN: return "misaligned pointer (16 B for tensors and codes, 4 B for alpha/amax)";
     case NVFP4_ERR_ALIAS: return "overlapping arguments";
     case NVFP4_ERR_HIP: return "HIP kernel launch failed";
+    case NVFP4_ERR_SCRATCH:
+      return "batch too large for the static scratch of the allocation-free call (E > 1024)";
   }
   return "unknown status";
 }
@@ -1641,6 +1675,23 @@ NVFP4_EXPORT nvfp4_status nvfp4_fakequant_fused(const uint16_t* in, int64_t E, i
                                                 uint32_t* workspace, hipStream_t stream) {
   return run_fused(in, E, rows, cols, block, mode, rule, nullptr, nullptr, out, out_alpha,
                    workspace, true, stream);
+}
+
+NVFP4_EXPORT nvfp4_status nvfp4_quantize_fused_noalloc(const uint16_t* in, int64_t E,
+                                                       int64_t rows, int64_t cols, int block,
+                                                       nvfp4_mode mode, nvfp4_rule rule,
+                                                       uint8_t* out_codes, uint8_t* out_scales,
+                                                       float* out_alpha, hipStream_t stream) {
+  Shape s;
+  const nvfp4_status st = validate_main(in, E, rows, cols, block, mode, rule, nullptr,
+                                        out_codes, out_scales, nullptr, out_alpha, false, &s);
+  if (st != NVFP4_OK) return st;
+  if (s.E > kScratchTensors) return NVFP4_ERR_SCRATCH;
+  uint32_t* ws = nullptr;
+  const nvfp4_status sst = scratch_on_current_device(&ws);
+  if (sst != NVFP4_OK) return sst;
+  return run_fused(in, E, rows, cols, block, mode, rule, out_codes, out_scales, nullptr,
+                   out_alpha, ws, false, stream);
 }
 
 NVFP4_EXPORT int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols,

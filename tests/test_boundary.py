@@ -20,7 +20,7 @@ import nvfp4_block_scaled_amax_amd as nv
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4_amax.h")
 
-OK, ENULL, ESHAPE, EBLOCK, EENUM, EALIGN, EHIP, EALIAS = range(8)
+OK, ENULL, ESHAPE, EBLOCK, EENUM, EALIGN, EHIP, EALIAS, ESCRATCH = range(9)
 
 
 @pytest.fixture(scope="module")
@@ -45,15 +45,15 @@ def test_header_declares_the_entry_points():
                             "nvfp4_fakequant_from_amax", "nvfp4_dequantize",
                             "nvfp4_quantize_diag", "nvfp4_quantize_fused",
                             "nvfp4_fakequant_fused", "nvfp4_fused_single_read",
-                            "nvfp4_fused_set_wait_limit"])
+                            "nvfp4_fused_set_wait_limit", "nvfp4_quantize_fused_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
     assert L.nvfp4_abi_version() == 5
-    for st in range(8):
-        assert L.nvfp4_status_str(st)
+    for st in range(9):
+        assert L.nvfp4_status_str(st) != b"unknown status"
     assert L.nvfp4_status_str(99) == b"unknown status"
 
 
@@ -163,6 +163,14 @@ def test_fused_validation(L):
     assert fq(A, 1, 4, 32, 16, 2, 0, B, C, D, W, None) == EENUM
     assert ff(A, 1, 4, 32, 16, 1, 0, B, D, None, None) == ENULL
     assert ff(A, 1, 4, 32, 16, 1, 0, B, D, B, None) == EALIAS              # over the output
+    # the allocation-free variant: the same validation, and at most 1024 tensors
+    fn = L.nvfp4_quantize_fused_noalloc
+    assert fn(A, 1, 4, 32, 16, 1, 0, B, C, None, None) == ENULL
+    assert fn(A, 1, 4, 30, 16, 1, 0, B, C, D, None) == ESHAPE
+    assert fn(A, 1, 4, 32, 16, 1, 0, A + 16, C, D, None) == EALIAS
+    assert fn(A, 1025, 1, 16, 16, 1, 0, B, C, D, None) == ESCRATCH
+    assert fn(A, 1025, 1, 16, 16, 3, 0, B, C, D, None) == EENUM   # argument errors come first
+    assert nv.NOALLOC_MAX_TENSORS == 1024
     # the shape query needs no GPU for argument errors
     assert L.nvfp4_fused_single_read(1, 4, 30, 1, 0, 0) == -ESHAPE
     assert L.nvfp4_fused_single_read(1, 4, 32, 3, 0, 0) == -EENUM
