@@ -296,14 +296,16 @@ __device__ __forceinline__ void fp4_pair(float xa, float xb, float r, float d, u
   }
 }
 
-// One candidate, table-driven: 8 code bytes in two words, returns the error.
+// One candidate, table-driven: 8 code bytes in two words, returns the error.  All four bytes
+// of each word are written below, so their start values (init0, init1) are irrelevant: the
+// caller passes values it no longer needs, so that the words need no register copies.
 template <int RULE>
 __device__ __forceinline__ float fast_candidate(const float (&x)[16], float r, float d,
-                                                uint32_t& w0, uint32_t& w1) {
+                                                uint32_t& w0, uint32_t& w1, uint32_t init0,
+                                                uint32_t init1) {
   float acc = 0.0f;
-  // all four bytes of each word are written below, so their start value is irrelevant
-  w0 = __float_as_uint(x[0]);
-  w1 = __float_as_uint(x[1]);
+  w0 = init0;
+  w1 = init1;
   fp4_pair<RULE, 0>(x[0], x[1], r, d, w0, acc);
   fp4_pair<RULE, 1>(x[2], x[3], r, d, w0, acc);
   fp4_pair<RULE, 2>(x[4], x[5], r, d, w0, acc);
@@ -314,6 +316,7 @@ __device__ __forceinline__ float fast_candidate(const float (&x)[16], float r, f
   fp4_pair<RULE, 3>(x[14], x[15], r, d, w1, acc);
   return acc;
 }
+
 
 // Per-tensor tables in LDS.
 //   D[s] = (d, r): the step d = RN(dec(s) * alpha) of E4M3 byte s and r = RN(1/d) (0 if d = 0)
@@ -371,12 +374,16 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
   // the range check below sends the block to the reference path.  rtn6 clamps at 448.
   const float sig6 = MODE == NVFP4_FOUR_OVER_SIX ? T.x * pe : fminf(T.x * pe, 448.0f);
   const float sig4 = MODE == NVFP4_FOUR_OVER_SIX ? T.y * pe : 0.0f;
-  const uint32_t sp = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sig6, sig4, 0, false);
+  slow = bb < 0x00800000u;   // block max below 2^-126 (or zero)
+  // the conversion writes the low 16 bits; the high half keeps bits of pe, which nothing reads
+  const uint32_t sp =
+      (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sig6, sig4, (int)__float_as_uint(pe), false);
   const uint32_t s6 = sp & 0xFFu;
   const f32x2 D6 = tb.D[s6];
-  slow = bb < 0x00800000u;   // block max below 2^-126 (or zero)
   four = false;
-  const float err6 = fast_candidate<RULE>(x, D6.y, D6.x, w0, w1);
+  const float err6 = fast_candidate<RULE>(
+      x, D6.y, D6.x, w0, w1, __float_as_uint(sig6),
+      __float_as_uint(MODE == NVFP4_FOUR_OVER_SIX ? sig4 : T.x));
   s = s6;
   d = D6.x;
   if (MODE == NVFP4_FOUR_OVER_SIX) {
@@ -387,7 +394,8 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
     // byte below 0x7E is within 1/16 of sigma, so the block max lands at most near 4.27.
     slow = slow || (s4 - 8u) >= 0x76u;
     uint32_t a4, b4;
-    const float err4 = fast_candidate<RULE>(x, D4.y, D4.x, a4, b4);
+    const float err4 = fast_candidate<RULE>(x, D4.y, D4.x, a4, b4, __float_as_uint(T.x),
+                                            __float_as_uint(T.y));
     if (err4 < err6) { s = s4; d = D4.x; w0 = a4; w1 = b4; four = true; }   // ties keep 6
   }
 }
@@ -1427,9 +1435,11 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
 
 // Tiers of blocks held per lane: (KR in VGPRs, KL in LDS) = (1,0), (4,0), (12,0), (20,8).  The
 // first tier that holds every tensor at once runs (more workgroups for smaller tensors).  A
-// batch that no tier holds at once runs in teams of (12,8) when one tensor fits: teams at
-// different tensors overlap loads with arithmetic.  Returns the blocks held per lane (1, 4,
-// 12, 28, or 20 for teams), or 0 when not even one tensor fits (the two-pass path).
+// batch that no tier holds at once runs in teams (kTeamSmallKR + 0 or kTeamKR + kTeamKL per
+// lane) when one tensor fits: teams at different tensors overlap loads with arithmetic.
+// Returns the blocks held per lane (1, 4, 12, 28, or 10 / 20 for teams), or 0 for the two-pass
+// path: when not even one tensor fits, and for a single Four Over Six tensor into packed
+// output beyond the 12-block tier (see below).
 template <int MODE, int RULE, bool FQ>
 int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uint8_t* codes,
                uint8_t* scales, uint16_t* out, float* alpha, hipStream_t stream) {
@@ -1446,6 +1456,13 @@ int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uin
   NVFP4_FUSED_TIER(1, 0, false)
   NVFP4_FUSED_TIER(4, 0, false)
   NVFP4_FUSED_TIER(12, 0, false)
+  // A single Four Over Six tensor into packed output that the tiers above do not hold takes
+  // the two-pass path: there the single read is not faster.  Its second phase (the two trials
+  // per block) cannot overlap the tensor's own loads, and costs what the second read costs
+  // (4096x14336: 50.2 against 50.5 us; 8192x4096: 34.3 against 34.0 us).  Fake-quant output,
+  // rtn6 and batches are faster read once (weight: 60.6 against 66.6 us fake-quant, 39.3
+  // against 50.5 us rtn6; three 4096x4096 tensors, 4/6 packed: 44.5 against 47.1 us).
+  if (MODE == NVFP4_FOUR_OVER_SIX && !FQ && s.E == 1) return 0;
   NVFP4_FUSED_TIER(20, 8, false)
   if (s.nblk < kTeamSmallBlocks) {
     NVFP4_FUSED_TIER(kTeamSmallKR, 0, true)

@@ -189,7 +189,8 @@ def test_diagnostics(nv, orc, shape, with_stats):
 
 # Single-read calls: every tier of blocks held per lane, and both team tiers.
 FUSED = [((256, 256), 1), ((1024, 4112), None), ((4096, 4112), None), ((4096, 14336), 28),
-         ((40, 256, 256), None), ((600, 256, 256), 10), ((6, 1024, 16384), 20)]
+         ((40, 256, 256), None), ((600, 256, 256), 10), ((6, 1024, 16384), 20),
+         ((3, 4096, 4096), None)]
 
 
 @pytest.mark.parametrize("shape,tier", FUSED, ids=[str(s) for s, _ in FUSED])
@@ -198,9 +199,11 @@ FUSED = [((256, 256), 1), ((1024, 4112), None), ((4096, 4112), None), ((4096, 14
 def test_fused(nv, orc, shape, tier, mode, rule, fq):
     got_tier = nv.fused_blocks_per_lane(shape, mode, rule, fq)
     say("[canary-fused] %s %s fq=%s: %d blocks per lane" % (shape, mode, fq, got_tier))
+    if shape == (4096, 14336) and not fq and mode == "four_over_six":
+        tier = 0                            # routed to the two-pass path
     if tier is not None:
         assert got_tier == tier
-    assert got_tier > 0
+    assert got_tier > 0 or tier == 0
     x = W.bits(W.generate("moe" if len(shape) == 3 else "weight", shape))
     E = shape[0] if len(shape) == 3 else 1
     xg = Guarded(shape, torch.bfloat16, init=bits_gpu(x))
