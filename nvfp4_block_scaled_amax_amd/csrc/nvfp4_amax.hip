@@ -181,19 +181,21 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //   - Four Over Six into packed output (two trials per block) needs its own loads in flight
 //     across its arithmetic.  Below 2^23 blocks (268 MB of input) 1024 workgroups in all
 //     (about 14 blocks per lane for the 4096x14336 weight) beat 4 blocks per lane by 3-5 %;
-//     from 2^23 blocks on, 4 blocks per lane beat 1024 or 768 workgroups by 4-12 % (MoE 10 %).
+//     from 2^23 blocks on, 4 blocks per lane beat 1024 or 768 workgroups by 4-12 % (MoE 10 %),
+//     and 3 blocks per lane beat 4 in four same-box A/B runs on three boxes: the 64-expert MoE
+//     batch 293.7-298.4 against 299.6-304.0 us, the 16384x14336 tensor 107.5-109.1 against
+//     109.5-110.3 us.  (2 per lane: faster than 3 on the 16384x14336 tensor in one run and
+//     slower on the MoE batch in another; 6 and 8: 4-10 % slower.)
 //   - The diagnostics variant ends with one or two same-address atomics per workgroup (the
 //     count of blocks scaled to 4, the statistics counter): 1024 workgroups in all.
 //   With paced waves (see the block-pass loop) the choices were measured again: 768, 1536 or
 //   2048 workgroups, 8 or 16 blocks per lane, 2048 or 4096 workgroups for long launches, and
-//   1024-4096 workgroups for rtn6 and fake-quant were all slower or equal.  For long launches
-//   2 or 6 blocks per lane were slower too; 3 measured 2-3 % faster on one box and 1-3 %
-//   slower on another, which is within the spread between boxes.  With the first loads issued
+//   1024-4096 workgroups for rtn6 and fake-quant were all slower or equal.  With the first loads issued
 //   at the kernel's start, 768, 1536 and 2048 workgroups measured 1-7 % slower than 1024 on
 //   the 4096x14336 weight.
 constexpr int64_t kLongLaunchBlocks = INT64_C(1) << 23;
 constexpr int64_t kShortLaunchWGs = 1024;
-constexpr int64_t kLaneBlocksLong = 4;
+constexpr int64_t kLaneBlocksLong = 3;
 constexpr int64_t kDiagLaunchWGs = 1024;
 constexpr uint32_t kPacedSteps = 8;      // grid-stride steps per lane from which waves pace themselves
 constexpr int kDiagCtrWords = 32;        // statistics workspace: one 128-byte counter line per tensor
