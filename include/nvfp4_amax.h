@@ -40,8 +40,9 @@
  *
  * Ownership and ordering: every pointer is a device pointer owned by the caller.  The
  * library allocates nothing.  Its only process-wide state is the wait limit of the
- * single-read calls (a test setting) and a per-device cache of occupancy figures, both
- * read and written atomically; calls are reentrant.  All work is
+ * single-read calls (a test setting) and per-device caches of device figures (occupancy and
+ * wall-clock rate) and of the allocation-free call's scratch address, all read
+ * and written atomically; calls are reentrant.  All work is
  * enqueued on `stream` (0 = the null stream) and the call returns at once; outputs are
  * defined once the stream passes the call.  During a dynamic-scale call out_alpha holds
  * the running amax, so it must not alias any other argument.  Fake-quant may run in
