@@ -279,14 +279,15 @@ __device__ __forceinline__ float max3_abs(float acc, float a, float b) {
 
 // One pair of elements of one candidate: v = x*r, FP4 round (hardware, round to nearest
 // even, saturating at 6, sign kept), decode, xhat = val*d, error into the running sum.
-// SEL (0..3) is the byte of the code word the pair lands in.
+// SEL (0..3) is the byte of the code word the pair lands in.  The two errors are also
+// returned (the statistics of the diagnostics variant use them; elsewhere they are dead).
 template <int RULE, int SEL>
 __device__ __forceinline__ void fp4_pair(float xa, float xb, float r, float d, uint32_t& word,
-                                         float& acc) {
+                                         float& acc, float& ea, float& eb) {
   word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, xa * r, xb * r, 1.0f, SEL);
   const f32x2 val = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
-  const float ea = xa - val.x * d;
-  const float eb = xb - val.y * d;
+  ea = xa - val.x * d;
+  eb = xb - val.y * d;
   if (RULE == NVFP4_RULE_MSE) {
     acc = __builtin_fmaf(ea, ea, acc);
     acc = __builtin_fmaf(eb, eb, acc);
@@ -304,18 +305,18 @@ __device__ __forceinline__ void fp4_pair(float xa, float xb, float r, float d, u
 template <int RULE>
 __device__ __forceinline__ float fast_candidate(const float (&x)[16], float r, float d,
                                                 uint32_t& w0, uint32_t& w1, uint32_t init0,
-                                                uint32_t init1) {
+                                                uint32_t init1, float (&e)[16]) {
   float acc = 0.0f;
   w0 = init0;
   w1 = init1;
-  fp4_pair<RULE, 0>(x[0], x[1], r, d, w0, acc);
-  fp4_pair<RULE, 1>(x[2], x[3], r, d, w0, acc);
-  fp4_pair<RULE, 2>(x[4], x[5], r, d, w0, acc);
-  fp4_pair<RULE, 3>(x[6], x[7], r, d, w0, acc);
-  fp4_pair<RULE, 0>(x[8], x[9], r, d, w1, acc);
-  fp4_pair<RULE, 1>(x[10], x[11], r, d, w1, acc);
-  fp4_pair<RULE, 2>(x[12], x[13], r, d, w1, acc);
-  fp4_pair<RULE, 3>(x[14], x[15], r, d, w1, acc);
+  fp4_pair<RULE, 0>(x[0], x[1], r, d, w0, acc, e[0], e[1]);
+  fp4_pair<RULE, 1>(x[2], x[3], r, d, w0, acc, e[2], e[3]);
+  fp4_pair<RULE, 2>(x[4], x[5], r, d, w0, acc, e[4], e[5]);
+  fp4_pair<RULE, 3>(x[6], x[7], r, d, w0, acc, e[6], e[7]);
+  fp4_pair<RULE, 0>(x[8], x[9], r, d, w1, acc, e[8], e[9]);
+  fp4_pair<RULE, 1>(x[10], x[11], r, d, w1, acc, e[10], e[11]);
+  fp4_pair<RULE, 2>(x[12], x[13], r, d, w1, acc, e[12], e[13]);
+  fp4_pair<RULE, 3>(x[14], x[15], r, d, w1, acc, e[14], e[15]);
   return acc;
 }
 
@@ -358,11 +359,15 @@ __device__ __forceinline__ void build_tables(BlockTables& tb, float alpha) {
 
 // Whole block: bmax, both candidate scales from the tables, both trials, selection.
 // Writes the chosen scale byte s, step d and code words; `slow` marks blocks that must be
-// redone on the reference path.
+// redone on the reference path.  For the diagnostics' statistics it also writes the chosen
+// candidate's errors e and its binary32 block scale sig = RN(bmax / RN(Q*alpha)) before the
+// E4M3 rounding and the clamp (valid for blocks not marked slow, while sig is normal); the
+// block pass leaves them unused and the compiler drops them.
 template <int MODE, int RULE>
 __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTables& tb,
                                            bool& slow, uint32_t& s, float& d,
-                                           uint32_t& w0, uint32_t& w1, float& bmax, bool& four) {
+                                           uint32_t& w0, uint32_t& w1, float& bmax, bool& four,
+                                           float (&e)[16], float& sig) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; i += 2) m = max3_abs(m, x[i], x[i + 1]);
@@ -374,7 +379,8 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
   // input by the hardware-conversion test).  For 4/6 that needs no clamp: the 4-scale is 1.5
   // times the 6-scale, so whenever either passes 448 the 4-scale byte is 0x7E or above, and
   // the range check below sends the block to the reference path.  rtn6 clamps at 448.
-  const float sig6 = MODE == NVFP4_FOUR_OVER_SIX ? T.x * pe : fminf(T.x * pe, 448.0f);
+  const float raw6 = T.x * pe;
+  const float sig6 = MODE == NVFP4_FOUR_OVER_SIX ? raw6 : fminf(raw6, 448.0f);
   const float sig4 = MODE == NVFP4_FOUR_OVER_SIX ? T.y * pe : 0.0f;
   slow = bb < 0x00800000u;   // block max below 2^-126 (or zero)
   // the conversion writes the low 16 bits; the high half keeps bits of pe, which nothing reads
@@ -385,9 +391,10 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
   four = false;
   const float err6 = fast_candidate<RULE>(
       x, D6.y, D6.x, w0, w1, __float_as_uint(sig6),
-      __float_as_uint(MODE == NVFP4_FOUR_OVER_SIX ? sig4 : T.x));
+      __float_as_uint(MODE == NVFP4_FOUR_OVER_SIX ? sig4 : T.x), e);
   s = s6;
   d = D6.x;
+  sig = raw6;
   if (MODE == NVFP4_FOUR_OVER_SIX) {
     const uint32_t s4 = (sp >> 8) & 0xFFu;
     const f32x2 D4 = tb.D[s4];
@@ -396,9 +403,14 @@ __device__ __forceinline__ void fast_block(const float (&x)[16], const BlockTabl
     // byte below 0x7E is within 1/16 of sigma, so the block max lands at most near 4.27.
     slow = slow || (s4 - 8u) >= 0x76u;
     uint32_t a4, b4;
+    float e4[16];
     const float err4 = fast_candidate<RULE>(x, D4.y, D4.x, a4, b4, __float_as_uint(T.x),
-                                            __float_as_uint(T.y));
-    if (err4 < err6) { s = s4; d = D4.x; w0 = a4; w1 = b4; four = true; }   // ties keep 6
+                                            __float_as_uint(T.y), e4);
+    if (err4 < err6) {                                                       // ties keep 6
+      s = s4; d = D4.x; w0 = a4; w1 = b4; four = true; sig = sig4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) e[i] = e4[i];
+    }
   }
 }
 
@@ -416,39 +428,57 @@ struct LaneStats {
   uint32_t near;
 };
 
-// The near-max test 3|x| > 2 bmax is taken as 1.5|x| > bmax in binary32: |x| is a bf16 value
-// (8 significant bits, exponent at least -133), so 1.5|x| is exact unless it overflows, and
-// an overflow means 1.5|x| exceeds every finite bmax, which the comparison with +inf also says.
-// Branch-free: the far elements add a zero to the near sum.
-template <int SEL>
-__device__ __forceinline__ void pair_stats(uint32_t w, float xa, float xb, float d, float bmax,
-                                           LaneStats& st) {
-  const f32x2 val = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);   // signed values
-  const float ea = xa - val.x * d;
-  const float eb = xb - val.y * d;
-  const double da = ea, db = eb;
-  st.sse = __builtin_fma(da, da, st.sse);
-  st.sse = __builtin_fma(db, db, st.sse);
-  st.sae = st.sae + __builtin_fabs(da);
-  st.sae = st.sae + __builtin_fabs(db);
-  st.mx = max3_abs(st.mx, ea, eb);
-  const bool na = 1.5f * fabsf(xa) > bmax, nb = 1.5f * fabsf(xb) > bmax;
-  const double na_e = na ? ea : 0.0f, nb_e = nb ? eb : 0.0f;
-  st.near_sse = __builtin_fma(na_e, na_e, st.near_sse);
-  st.near_sse = __builtin_fma(nb_e, nb_e, st.near_sse);
-  st.near += (uint32_t)na + (uint32_t)nb;
+// The near-max band is 3|x| > 2 bmax.  |x| and bmax are bf16 values, and for those the test
+// equals |x| > t with the per-block threshold t = RN(bmax * RN(2/3)) with its low 16 bits
+// cleared: 2 bmax / 3 is either a bf16 value, which the product then rounds to exactly, or
+// lies at least a third of a bf16 step away from the nearest bf16 values, so that the
+// product (within 2^-23 of it, relatively) truncates to the bf16 value just below it.  (A
+// test checks the equivalence for every pair of bf16 magnitudes |x| <= bmax.)
+__device__ __forceinline__ float near_threshold(float bmax) {
+  return __uint_as_float(__float_as_uint(bmax * 0.6666667f) & 0xFFFF0000u);
 }
 
-__device__ __forceinline__ void chosen_stats(const float (&x)[16], uint32_t w0, uint32_t w1,
-                                             float d, float bmax, LaneStats& st) {
-  pair_stats<0>(w0, x[0], x[1], d, bmax, st);
-  pair_stats<1>(w0, x[2], x[3], d, bmax, st);
-  pair_stats<2>(w0, x[4], x[5], d, bmax, st);
-  pair_stats<3>(w0, x[6], x[7], d, bmax, st);
-  pair_stats<0>(w1, x[8], x[9], d, bmax, st);
-  pair_stats<1>(w1, x[10], x[11], d, bmax, st);
-  pair_stats<2>(w1, x[12], x[13], d, bmax, st);
-  pair_stats<3>(w1, x[14], x[15], d, bmax, st);
+// Statistics of one block from its elements x and the chosen candidate's errors e (exact in
+// binary32, so each e^2 is exact in binary64).  Branch-free: the far elements add a zero to
+// the near sum.
+__device__ __forceinline__ void block_stats(const float (&x)[16], const float (&e)[16],
+                                            float tnear, LaneStats& st) {
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const double da = e[i], db = e[i + 1];
+    st.sse = __builtin_fma(da, da, st.sse);
+    st.sse = __builtin_fma(db, db, st.sse);
+    st.sae = st.sae + __builtin_fabs(da);
+    st.sae = st.sae + __builtin_fabs(db);
+    st.mx = max3_abs(st.mx, e[i], e[i + 1]);
+    const bool na = fabsf(x[i]) > tnear, nb = fabsf(x[i + 1]) > tnear;
+    const double na_e = na ? e[i] : 0.0f, nb_e = nb ? e[i + 1] : 0.0f;
+    st.near_sse = __builtin_fma(na_e, na_e, st.near_sse);
+    st.near_sse = __builtin_fma(nb_e, nb_e, st.near_sse);
+    st.near += (uint32_t)na + (uint32_t)nb;
+  }
+}
+
+// The chosen candidate's errors recomputed from its codes and step d (for the blocks that
+// the reference path redid): e = x - val*d, with the signed values the codes decode to.
+template <int SEL>
+__device__ __forceinline__ void pair_errors(uint32_t w, float xa, float xb, float d, float& ea,
+                                            float& eb) {
+  const f32x2 val = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  ea = xa - val.x * d;
+  eb = xb - val.y * d;
+}
+
+__device__ __forceinline__ void chosen_errors(const float (&x)[16], uint32_t w0, uint32_t w1,
+                                              float d, float (&e)[16]) {
+  pair_errors<0>(w0, x[0], x[1], d, e[0], e[1]);
+  pair_errors<1>(w0, x[2], x[3], d, e[2], e[3]);
+  pair_errors<2>(w0, x[4], x[5], d, e[4], e[5]);
+  pair_errors<3>(w0, x[6], x[7], d, e[6], e[7]);
+  pair_errors<0>(w1, x[8], x[9], d, e[8], e[9]);
+  pair_errors<1>(w1, x[10], x[11], d, e[10], e[11]);
+  pair_errors<2>(w1, x[12], x[13], d, e[12], e[13]);
+  pair_errors<3>(w1, x[14], x[15], d, e[14], e[15]);
 }
 
 // Sum of e^2 of one block when the chosen candidate (cq = RN(Q*alpha), capv its largest FP4
@@ -470,10 +500,15 @@ __device__ __noinline__ double f32_scale_sse_div(const uint16_t* __restrict__ xb
   return acc;
 }
 
+// sig_t is the fast path's table product for the chosen candidate; table_ok says it equals
+// RN(bmax / cq) (a block the fast path kept, with a normal product), else the quotient is
+// formed here.
 __device__ __forceinline__ double f32_scale_sse(const float (&x)[16],
                                                 const uint16_t* __restrict__ xb, float bmax,
-                                                float alpha, float cq, float capv) {
-  const float sigma = alpha == 0.0f ? 0.0f : bmax / cq;
+                                                float alpha, float cq, float capv, float sig_t,
+                                                bool table_ok) {
+  float sigma = sig_t;
+  if (!table_ok) sigma = alpha == 0.0f ? 0.0f : bmax / cq;
   const float d = sigma * alpha;
   const float r = d == 0.0f ? 0.0f : 1.0f / d;
   if (r == __builtin_inff()) return f32_scale_sse_div(xb, d, capv);
@@ -552,8 +587,11 @@ __device__ __forceinline__ void dequant_bf16(uint32_t w0, uint32_t w1, float d, 
 // the current step's arithmetic.  Block indices are 32-bit (the host splits tensors of 2^27
 // blocks or more into launches below that), so every access is a uniform 64-bit base plus a
 // 32-bit lane offset.  DIAG (packed output only) also writes, per block, the block maximum
-// it was scaled to (4 or 6) and counts the blocks scaled to 4 per tensor.
-template <int MODE, int RULE, bool FQ, bool DIAG>
+// it was scaled to (4 or 6) and counts the blocks scaled to 4 per tensor; DIAG == kDiagStats
+// also reduces the error statistics (a variant of its own: keeping the chosen candidate's
+// errors for them costs registers that the call without statistics should not pay).
+constexpr int kDiagPlain = 1, kDiagStats = 2;
+template <int MODE, int RULE, bool FQ, int DIAG>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     const uint4* __restrict__ in, int64_t nblk, const float* __restrict__ amax,
@@ -604,7 +642,7 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   }
   uint32_t n_four = 0;   // DIAG: blocks of this lane scaled to 4
   LaneStats st = {0.0, 0.0, 0.0, 0.0, 0.0f, 0u};
-  const bool want_stats = DIAG && stats != nullptr;
+  constexpr bool want_stats = DIAG == kDiagStats;   // stats and its workspaces are then set
 
   build_tables<MODE>(tb, alpha);
   __syncthreads();
@@ -636,10 +674,11 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
     float x[16];
     unpack16(c0, c1, x);
     uint32_t sc, w0, w1;
-    float dq, bm;
+    float dq, bm, e[16], sg;
     bool slow, four;
-    fast_block<MODE, RULE>(x, tb, slow, sc, dq, w0, w1, bm, four);
-    if (slow || tiny_alpha) {        // rare: redo the block on the reference path
+    fast_block<MODE, RULE>(x, tb, slow, sc, dq, w0, w1, bm, four, e, sg);
+    const bool redo = slow || tiny_alpha;
+    if (redo) {                      // rare: redo the block on the reference path
       const RefOut o =
           ref_block<MODE, RULE>(reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm, alpha);
       sc = o.s;
@@ -658,10 +697,11 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
         qstar[base + u] = four ? 4 : 6;
         n_four += four ? 1u : 0u;
         if (want_stats) {
-          chosen_stats(x, w0, w1, dq, bm, st);
+          if (redo) chosen_errors(x, w0, w1, dq, e);
+          block_stats(x, e, near_threshold(bm), st);
           st.f32_sse += f32_scale_sse(x, reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm,
                                       alpha, four ? 4.0f * alpha : 6.0f * alpha,
-                                      four ? 4.0f : 6.0f);
+                                      four ? 4.0f : 6.0f, sg, !redo && sg >= 0x1p-126f);
         }
       }
     }
@@ -853,9 +893,9 @@ __device__ __forceinline__ void fused_emit(const uint4& c0, const uint4& c1, uin
   float x[16];
   unpack16(c0, c1, x);
   uint32_t sc, w0, w1;
-  float dq, bm;
+  float dq, bm, e_unused[16], sg_unused;
   bool slow, four;
-  fast_block<MODE, RULE>(x, tb, slow, sc, dq, w0, w1, bm, four);
+  fast_block<MODE, RULE>(x, tb, slow, sc, dq, w0, w1, bm, four, e_unused, sg_unused);
   if (slow || tiny_alpha) {
     const RefOut o =
         ref_block<MODE, RULE>(reinterpret_cast<const uint16_t*>(inT + (u << 5)), bm, alpha);
@@ -1186,7 +1226,7 @@ hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStr
 
 constexpr int64_t kMaxLaunchBlocks = (INT64_C(1) << 27) - 1;   // 32-bit byte offsets in kernels
 
-template <int MODE, int RULE, bool FQ, bool DIAG>
+template <int MODE, int RULE, bool FQ, int DIAG>
 void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, uint8_t* codes,
                        uint8_t* scales, uint16_t* out, float* alpha_out, uint8_t* qstar,
                        uint32_t* count4, double* stats, uint32_t* stats_ws, hipStream_t stream) {
@@ -1224,7 +1264,7 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
   }
 }
 
-template <bool FQ, bool DIAG>
+template <bool FQ, int DIAG>
 void launch_quantize(int mode, int rule, const uint16_t* in, const Shape& s, const float* amax,
                      uint8_t* codes, uint8_t* scales, uint16_t* out, float* alpha_out,
                      uint8_t* qstar, uint32_t* count4, double* stats, uint32_t* stats_ws,
@@ -1342,13 +1382,16 @@ nvfp4_status run(const uint16_t* in, int64_t E, int64_t rows, int64_t cols, int 
   // when alpha doubles as the amax accumulator a follow-up kernel converts it in place.
   float* alpha_in_kernel = amax == alpha ? nullptr : alpha;
   if (fq)
-    launch_quantize<true, false>(mode, rule, in, s, amax, nullptr, nullptr, out, alpha_in_kernel,
+    launch_quantize<true, 0>(mode, rule, in, s, amax, nullptr, nullptr, out, alpha_in_kernel,
                                  nullptr, nullptr, nullptr, nullptr, stream);
+  else if (diag && stats)
+    launch_quantize<false, kDiagStats>(mode, rule, in, s, amax, codes, scales, nullptr,
+                                       alpha_in_kernel, qstar, count4, stats, stats_ws, stream);
   else if (diag)
-    launch_quantize<false, true>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
-                                 qstar, count4, stats, stats ? stats_ws : nullptr, stream);
+    launch_quantize<false, kDiagPlain>(mode, rule, in, s, amax, codes, scales, nullptr,
+                                       alpha_in_kernel, qstar, count4, nullptr, nullptr, stream);
   else
-    launch_quantize<false, false>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
+    launch_quantize<false, 0>(mode, rule, in, s, amax, codes, scales, nullptr, alpha_in_kernel,
                                   nullptr, nullptr, nullptr, nullptr, stream);
   if (hipGetLastError() != hipSuccess) return NVFP4_ERR_HIP;
   if (!alpha_in_kernel &&
