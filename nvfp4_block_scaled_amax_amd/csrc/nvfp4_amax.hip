@@ -863,23 +863,41 @@ constexpr int64_t kFusedMaxTensorWGs = 512;           // see fused_tier_wgs
 // the larger team tier measured equal or faster (the 64-expert MoE batch: 452 against 526 us).
 constexpr int64_t kTeamSmallBlocks = INT64_C(1) << 18;
 constexpr int kTeamSmallKR = 10;
+// Four Over Six into packed output (from kTeamSmallBlocks on) runs its teams with wider
+// workgroups: kTeamWideKR blocks per lane in VGPRs, none in LDS, at most 128 VGPRs, so that a
+// workgroup of 512 threads puts 2 waves on each SIMD and two of them share a CU; or one of 1024
+// threads, 4 waves per SIMD, one per CU.  The block pass of a held tensor needs about four
+// waves per SIMD to keep the VALU issuing (two per SIMD issue about half as fast), and the two
+// workgroups that share a CU (workgroups i and i + #CUs) should compute at the same time,
+// which the odd/even start of the teams gives when there are at least four teams (teams y and
+// y + T/2 share CUs).  With fewer, the 1024-thread form keeps every CU in one team.  Same-box
+// A/B (4/6-MSE packed, us per call; 18 + 2 at 256 threads / 512 threads / 1024 threads):
+// 64x2048x5120 (4 teams) 418 / 389 / 405; 40x2048x6144 (3) 376 / 352 / 366; 24x3072x4096 (3)
+// 224 / 216 / 210; 96x1024x4096 (9) 279 / 273 / 274; 16x2048x8192 (2) 215 / 211 / 176;
+// 12x4096x4096 (2) 165 / 154 / 135.  rtn6 and fake-quant output keep the 18 + 2 tier: there
+// the wide tiers measured equal or slower (rtn6 on the MoE batch 352 / 353 / 384 us, rtn6
+// fake-quant 518 / 561 / 528 us, 4/6-MAE fake-quant 547 / 556 / 586 us).
+constexpr int kTeamWideKR = 10;
+constexpr int64_t kTeamWideMinTeams = 3;
 constexpr int kFusedGroups = 16;
 constexpr int kLineWords = 32;                           // 128 bytes
 constexpr int64_t kFusedWsWords = (kFusedGroups + 1) * kLineWords;
 static_assert(kFusedWsWords == NVFP4_FUSED_WS_WORDS, "workspace size of the fused calls");
 
-// Magnitude max of tensor t computed by one workgroup alone (the fallback of the wait).
+// Magnitude max of tensor t computed by one workgroup of NT threads alone (the fallback of the
+// wait).
+template <int NT>
 __device__ __noinline__ uint32_t wg_tensor_amax(const uint4* __restrict__ p, int64_t chunks,
                                                 uint32_t* part) {
   uint32_t m = 0;
-  for (int64_t i = threadIdx.x; i < chunks; i += kThreads) m = mag_max8(m, p[i]);
+  for (int64_t i = threadIdx.x; i < chunks; i += NT) m = mag_max8(m, p[i]);
   m = max(m & 0xFFFFu, m >> 16) << 16;
   m = wave_max_u32(m);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
   uint32_t r = part[0];
-  for (int w = 1; w < kThreads / 64; ++w) r = max(r, part[w]);
+  for (int w = 1; w < NT / 64; ++w) r = max(r, part[w]);
   __syncthreads();   // every wave has read part[] before any reuses it (the next tensor)
   return r;
 }
@@ -927,15 +945,16 @@ __device__ __forceinline__ void fused_poison(uint32_t u, char* codesT, uint8_t* 
   }
 }
 
-// One tensor t of a fused launch (x = G workgroups per tensor): phase 1, the grid-wide wait,
-// phase 2.  nblk <= (KR + KL) * G * 256 per tensor and nblk < 2^27 (the host checks both).
-template <int MODE, int RULE, bool FQ, int KR, int KL>
+// One tensor t of a fused launch (x = G workgroups of NT threads per tensor): phase 1, the
+// grid-wide wait, phase 2.  nblk <= (KR + KL) * G * NT per tensor and nblk < 2^27 (the host
+// checks both).
+template <int MODE, int RULE, bool FQ, int KR, int KL, int NT>
 __device__ __forceinline__ void fused_tensor(
     int64_t t, uint32_t tid, const uint4* __restrict__ in, int64_t nblk,
     uint32_t* __restrict__ ws, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
     uint4* __restrict__ out, float* __restrict__ alpha_out, uint32_t wait_polls,
     uint64_t wait_ticks, BlockTables& tb,
-    uint4 (&held)[KL > 0 ? KL : 1][2][kThreads], uint32_t* part, uint32_t& amax_sh) {
+    uint4 (&held)[KL > 0 ? KL : 1][2][NT], uint32_t* part, uint32_t& amax_sh) {
   const uint32_t G = gridDim.x, g = blockIdx.x;
   const uint32_t n = (uint32_t)nblk;
   const int64_t base = t * nblk;
@@ -948,7 +967,7 @@ __device__ __forceinline__ void fused_tensor(
   uint4 r0[KR], r1[KR], l0[KL > 0 ? KL : 1], l1[KL > 0 ? KL : 1];
 #pragma unroll
   for (int k = 0; k < KR; ++k) {
-    const uint32_t u = ((uint32_t)k * G + g) * kThreads + tid;
+    const uint32_t u = ((uint32_t)k * G + g) * NT + tid;
     r0[k] = r1[k] = make_uint4(0u, 0u, 0u, 0u);
     if (u < n) {
       r0[k] = *reinterpret_cast<const uint4*>(inT + (u << 5));
@@ -957,7 +976,7 @@ __device__ __forceinline__ void fused_tensor(
   }
 #pragma unroll
   for (int k = 0; k < KL; ++k) {
-    const uint32_t u = ((uint32_t)(KR + k) * G + g) * kThreads + tid;
+    const uint32_t u = ((uint32_t)(KR + k) * G + g) * NT + tid;
     l0[k] = l1[k] = make_uint4(0u, 0u, 0u, 0u);
     if (u < n) {
       l0[k] = *reinterpret_cast<const uint4*>(inT + (u << 5));
@@ -981,7 +1000,7 @@ __device__ __forceinline__ void fused_tensor(
   // arrival and the grid-wide wait (one lane), bounded
   if (tid == 0) {
     uint32_t wgm = part[0];
-    for (int w = 1; w < kThreads / 64; ++w) wgm = max(wgm, part[w]);
+    for (int w = 1; w < NT / 64; ++w) wgm = max(wgm, part[w]);
     // groups of at least 8 workgroups, at most 16 groups; one group needs no top level.  Up
     // to 16 workgroups meet on one line (measured 11 % faster for the 16-workgroup 256x256
     // call); 128 workgroups on one line measured 1.5x slower than 16 groups of 8.
@@ -1030,7 +1049,7 @@ __device__ __forceinline__ void fused_tensor(
   __syncthreads();
   uint32_t abits = amax_sh;
   if (abits == 0xFFFFFFFFu)
-    abits = wg_tensor_amax(reinterpret_cast<const uint4*>(inT), nblk * 2, part);
+    abits = wg_tensor_amax<NT>(reinterpret_cast<const uint4*>(inT), nblk * 2, part);
 
   // phase 2: the block pass on the held blocks
   const bool poison = abits >= 0x7F800000u;
@@ -1040,7 +1059,7 @@ __device__ __forceinline__ void fused_tensor(
   if (poison) {
 #pragma unroll
     for (int k = 0; k < KR + KL; ++k) {
-      const uint32_t u = ((uint32_t)k * G + g) * kThreads + tid;
+      const uint32_t u = ((uint32_t)k * G + g) * NT + tid;
       if (u < n) fused_poison<FQ>(u, codesT, scalesT, outT);
     }
     return;
@@ -1058,7 +1077,7 @@ __device__ __forceinline__ void fused_tensor(
     if (pace && k == K / 4) __builtin_amdgcn_s_setprio(2);
     if (pace && k == K / 2) __builtin_amdgcn_s_setprio(1);
     if (pace && k == (3 * K) / 4) __builtin_amdgcn_s_setprio(0);
-    const uint32_t u = ((uint32_t)k * G + g) * kThreads + tid;
+    const uint32_t u = ((uint32_t)k * G + g) * NT + tid;
     if (u < n)
       fused_emit<MODE, RULE, FQ>(r0[k], r1[k], u, inT, codesT, scalesT, outT, tb,
                                  alpha, tiny_alpha);
@@ -1068,7 +1087,7 @@ __device__ __forceinline__ void fused_tensor(
     if (pace && KR + k == K / 4) __builtin_amdgcn_s_setprio(2);
     if (pace && KR + k == K / 2) __builtin_amdgcn_s_setprio(1);
     if (pace && KR + k == (3 * K) / 4) __builtin_amdgcn_s_setprio(0);
-    const uint32_t u = ((uint32_t)(KR + k) * G + g) * kThreads + tid;
+    const uint32_t u = ((uint32_t)(KR + k) * G + g) * NT + tid;
     if (u < n)
       fused_emit<MODE, RULE, FQ>(held[k][0][tid], held[k][1][tid], u, inT, codesT, scalesT,
                                  outT, tb, alpha, tiny_alpha);
@@ -1081,17 +1100,19 @@ __device__ __forceinline__ void fused_tensor(
 // arithmetic.  Between tensors a team needs no barrier of its own: a workgroup's threads reuse
 // only their own held blocks, and the shared tables and flags are rewritten only after the next
 // tensor's phase-1 barriers, which every thread of the workgroup reaches after its phase 2.
-template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fused_kernel(
+// NT threads per workgroup: 256, or 512 and 1024 for the Four Over Six team tiers below (at
+// most 128 VGPRs, so that 4 waves per SIMD fit).
+template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT > 256 ? 4 : 2))) void fused_kernel(
     const uint4* __restrict__ in, int64_t nblk, uint32_t* __restrict__ ws,
     uint2* __restrict__ codes, uint8_t* __restrict__ scales, uint4* __restrict__ out,
     float* __restrict__ alpha_out, uint32_t wait_polls, uint64_t wait_ticks, int64_t E) {
   __shared__ BlockTables tb;
-  __shared__ uint4 held[KL > 0 ? KL : 1][2][kThreads];
-  __shared__ uint32_t part[kThreads / 64];
+  __shared__ uint4 held[KL > 0 ? KL : 1][2][NT];
+  __shared__ uint32_t part[NT / 64];
   __shared__ uint32_t amax_sh;
   if (!TEAMS) {
-    fused_tensor<MODE, RULE, FQ, KR, KL>(blockIdx.y, threadIdx.x, in, nblk, ws, codes, scales, out,
+    fused_tensor<MODE, RULE, FQ, KR, KL, NT>(blockIdx.y, threadIdx.x, in, nblk, ws, codes, scales, out,
                                          alpha_out, wait_polls, wait_ticks, tb, held, part,
                                          amax_sh);
     return;
@@ -1114,7 +1135,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // from hoisting them out of the loop, where they would stay live in registers.
     uint32_t tid;
     asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(threadIdx.x));
-    fused_tensor<MODE, RULE, FQ, KR, KL>(t, tid, in, nblk, ws, codes, scales, out, alpha_out,
+    fused_tensor<MODE, RULE, FQ, KR, KL, NT>(t, tid, in, nblk, ws, codes, scales, out, alpha_out,
                                          wait_polls, wait_ticks, tb, held, part, amax_sh);
   }
 }
@@ -1427,7 +1448,7 @@ uint64_t fused_wait_ticks(const Shape& s, int64_t at_once) {
 
 // Workgroups of one fused_kernel instance that fit on the current device at once (occupancy
 // per CU times the CU count), cached per device; 0 if unknown.
-template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS>
+template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS, int NT>
 int64_t fused_resident_wgs() {
   static std::atomic<int64_t> cache[64];
   int dev = 0;
@@ -1437,8 +1458,8 @@ int64_t fused_resident_wgs() {
   int per_cu = 0, cus = 0;
   const bool ok =
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&fused_kernel<MODE, RULE, FQ, KR, KL, TEAMS>),
-          kThreads,
+          &per_cu, reinterpret_cast<const void*>(&fused_kernel<MODE, RULE, FQ, KR, KL, TEAMS, NT>),
+          NT,
           0) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
   v = ok ? (int64_t)per_cu * cus : 0;
@@ -1460,11 +1481,11 @@ int64_t fused_resident_wgs() {
 //     against teams of exactly G: 18-20 % faster on batches of 524,288-block tensors (where 4
 //     teams of 103 workgroups left 100 of 512 slots idle), 6-9 % on 262,144- and
 //     1,048,576-block tensors.
-template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS>
+template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS, int NT>
 int64_t fused_tier_wgs(const Shape& s, int64_t* teams) {
-  constexpr int64_t per_wg = (int64_t)(KR + KL) * kThreads;
+  constexpr int64_t per_wg = (int64_t)(KR + KL) * NT;
   const int64_t G = (s.nblk + per_wg - 1) / per_wg;
-  const int64_t resident = fused_resident_wgs<MODE, RULE, FQ, KR, KL, TEAMS>();
+  const int64_t resident = fused_resident_wgs<MODE, RULE, FQ, KR, KL, TEAMS, NT>();
   if (!TEAMS) {
     *teams = (G * s.E <= resident && G <= kFusedMaxTensorWGs) ? s.E : 0;
     return (KR + KL >= 12 && *teams > 0) ? std::max(G, resident / s.E) : G;
@@ -1474,7 +1495,7 @@ int64_t fused_tier_wgs(const Shape& s, int64_t* teams) {
   return T > 0 ? std::max(G, resident / T) : G;
 }
 
-template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS>
+template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS, int NT>
 void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint32_t* ws,
                   uint8_t* codes, uint8_t* scales, uint16_t* out, float* alpha,
                   hipStream_t stream) {
@@ -1482,8 +1503,8 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((words + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, stream, ws, nullptr, words, nullptr, (int64_t)0, nullptr,
                      (int64_t)0);
-  hipLaunchKernelGGL((fused_kernel<MODE, RULE, FQ, KR, KL, TEAMS>), dim3((unsigned)G, (unsigned)T),
-                     dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(in), s.nblk, ws,
+  hipLaunchKernelGGL((fused_kernel<MODE, RULE, FQ, KR, KL, TEAMS, NT>), dim3((unsigned)G, (unsigned)T),
+                     dim3(NT), 0, stream, reinterpret_cast<const uint4*>(in), s.nblk, ws,
                      reinterpret_cast<uint2*>(codes), scales, reinterpret_cast<uint4*>(out), alpha,
                      g_wait_polls.load(std::memory_order_relaxed), fused_wait_ticks(s, T),
                      s.E);
@@ -1491,27 +1512,27 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
 
 // Tiers of blocks held per lane: (KR in VGPRs, KL in LDS) = (1,0), (4,0), (12,0), (20,8).  The
 // first tier that holds every tensor at once runs (more workgroups for smaller tensors).  A
-// batch that no tier holds at once runs in teams (kTeamSmallKR + 0 or kTeamKR + kTeamKL per
-// lane) when one tensor fits: teams at different tensors overlap loads with arithmetic.
-// Returns the blocks held per lane (1, 4, 12, 28, or 10 / 20 for teams), or 0 for the two-pass
-// path: when not even one tensor fits, and for a single Four Over Six tensor into packed
-// output beyond the 12-block tier (see below).
+// batch that no tier holds at once runs in teams (kTeamSmallKR + 0, kTeamWideKR + 0 or
+// kTeamKR + kTeamKL per lane) when one tensor fits: teams at different tensors overlap loads
+// with arithmetic.  Returns the blocks held per lane (1, 4, 12, 28, or 10 / 20 for teams), or 0
+// for the two-pass path: when not even one tensor fits, and for a single Four Over Six tensor
+// into packed output beyond the 12-block tier (see below).
 template <int MODE, int RULE, bool FQ>
 int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uint8_t* codes,
                uint8_t* scales, uint16_t* out, float* alpha, hipStream_t stream) {
   if (s.nblk > kMaxLaunchBlocks) return 0;
   int64_t G, T;
-#define NVFP4_FUSED_TIER(KR, KL, TEAMS)                                                         \
-  G = fused_tier_wgs<MODE, RULE, FQ, KR, KL, TEAMS>(s, &T);                                   \
+#define NVFP4_FUSED_TIER(KR, KL, TEAMS, NT)                                                     \
+  G = fused_tier_wgs<MODE, RULE, FQ, KR, KL, TEAMS, NT>(s, &T);                               \
   if (T > 0) {                                                                                \
     if (launch)                                                                               \
-      fused_launch<MODE, RULE, FQ, KR, KL, TEAMS>(G, T, in, s, ws, codes, scales, out, alpha,   \
-                                                  stream);                                    \
+      fused_launch<MODE, RULE, FQ, KR, KL, TEAMS, NT>(G, T, in, s, ws, codes, scales, out,      \
+                                                      alpha, stream);                         \
     return KR + KL;                                                                           \
   }
-  NVFP4_FUSED_TIER(1, 0, false)
-  NVFP4_FUSED_TIER(4, 0, false)
-  NVFP4_FUSED_TIER(12, 0, false)
+  NVFP4_FUSED_TIER(1, 0, false, kThreads)
+  NVFP4_FUSED_TIER(4, 0, false, kThreads)
+  NVFP4_FUSED_TIER(12, 0, false, kThreads)
   // A single Four Over Six tensor into packed output that the tiers above do not hold takes
   // the two-pass path: there the single read is not faster.  Its second phase (the two trials
   // per block) cannot overlap the tensor's own loads, and costs what the second read costs
@@ -1519,11 +1540,20 @@ int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uin
   // rtn6 and batches are faster read once (weight: 60.6 against 66.6 us fake-quant, 39.3
   // against 50.5 us rtn6; three 4096x4096 tensors, 4/6 packed: 44.5 against 47.1 us).
   if (MODE == NVFP4_FOUR_OVER_SIX && !FQ && s.E == 1) return 0;
-  NVFP4_FUSED_TIER(20, 8, false)
+  NVFP4_FUSED_TIER(20, 8, false, kThreads)
   if (s.nblk < kTeamSmallBlocks) {
-    NVFP4_FUSED_TIER(kTeamSmallKR, 0, true)
+    NVFP4_FUSED_TIER(kTeamSmallKR, 0, true, kThreads)
   }
-  NVFP4_FUSED_TIER(kTeamKR, kTeamKL, true)
+  if constexpr (MODE == NVFP4_FOUR_OVER_SIX && !FQ) {
+    // wide workgroups: 512 threads when that gives at least kTeamWideMinTeams teams, else 1024
+    int64_t T512 = 0;
+    fused_tier_wgs<MODE, RULE, FQ, kTeamWideKR, 0, true, 512>(s, &T512);
+    if (T512 >= kTeamWideMinTeams) {
+      NVFP4_FUSED_TIER(kTeamWideKR, 0, true, 512)
+    }
+    NVFP4_FUSED_TIER(kTeamWideKR, 0, true, 1024)
+  }
+  NVFP4_FUSED_TIER(kTeamKR, kTeamKL, true, kThreads)
 #undef NVFP4_FUSED_TIER
   return 0;
 }

@@ -3,7 +3,8 @@
 The fused entry points must give the dynamic entry points' results bit for bit: codes, scale
 bytes, alpha bits and fake-quant bf16 bits equal to the oracle's.  Covered here: every tier of
 blocks held per lane (1, 4, 12 and 28, confirmed through the shape query), the batched form,
-batches run in teams (20 per lane; the 64-expert MoE batch whole),
+batches run in teams (10 or 20 per lane, in workgroups of 256, 512 or 1024 threads; the 64-expert
+MoE batch whole),
 the edge tensors, poisoning, the bounded grid-wide wait forced from the host (every workgroup
 or some of them computing the tensor amax alone), the two-pass route for tensors that do not
 fit on chip and for in-place fake-quant, and a workspace that starts with arbitrary content."""
@@ -155,9 +156,11 @@ def test_fused_bounded_wait_fallback(nv, orc, limit, shape):
 
 
 # Batches that no tier holds at once but whose single tensors fit: teams of workgroups take the
-# tensors in turn (20 blocks per lane, 10 for tensors under 262,144 blocks; odd teams start half
-# a cycle late).
-TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),
+# tensors in turn (odd teams start half a cycle late).  10 blocks per lane for tensors under
+# 262,144 blocks and for Four Over Six into packed output (in 512-thread workgroups when that
+# gives at least three teams, else 1024-thread ones), 20 otherwise.
+TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),     # 2 teams of 1024 threads
+         ((10, 1024, 8192), "four_over_six", "mse", False),     # 4 teams of 512 threads
          ((5, 1000, 14336), "four_over_six", "mae", True),
          ((12, 512, 14336), "rtn6", "mse", False),
          ((3, 2048, 14336), "four_over_six", "maxerr", False),
@@ -165,11 +168,16 @@ TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),
          ((700, 128, 512), "four_over_six", "mae", True)]
 
 
+def team_tier(shape, mode, fq):
+    small = shape[1] * shape[2] // 16 < 2 ** 18
+    return 10 if small or (mode == "four_over_six" and not fq) else 20
+
+
 @pytest.mark.parametrize("shape,mode,rule,fq", TEAMS, ids=["t%d" % i for i in range(len(TEAMS))])
 def test_fused_teams_whole_batch(nv, orc, shape, mode, rule, fq):
     tier = nv.fused_blocks_per_lane(shape, mode, rule, fq)
     say("[fused-teams] %s %s/%s fq=%s: %d blocks per lane" % (shape, mode, rule, fq, tier))
-    assert tier == (10 if shape[1] * shape[2] // 16 < 2 ** 18 else 20), tier
+    assert tier == team_tier(shape, mode, fq), tier
     x = W.bits(W.generate("moe", shape))
     assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq, str(shape))
 
@@ -190,7 +198,7 @@ def test_fused_teams_bounded_wait(nv, orc, limit):
 def test_fused_teams_moe_full_size(nv, orc):
     """The 64-expert MoE tensor (2048 x 5120 per expert), read once, whole against the oracle."""
     shape = W.WORKLOADS["moe"].shape
-    assert nv.fused_blocks_per_lane(shape, "four_over_six", "mse", False) == 20
+    assert nv.fused_blocks_per_lane(shape, "four_over_six", "mse", False) == 10
     xt = W.generate("moe")
     say("[fused-teams] moe %s" % (shape,))
     c, s, a = nv.quantize_fused(xt.cuda(), "four_over_six", "mse")
