@@ -1488,7 +1488,7 @@ int64_t fused_tier_wgs(const Shape& s, int64_t* teams) {
   const int64_t resident = fused_resident_wgs<MODE, RULE, FQ, KR, KL, TEAMS, NT>();
   if (!TEAMS) {
     *teams = (G * s.E <= resident && G <= kFusedMaxTensorWGs) ? s.E : 0;
-    return (KR + KL >= 12 && *teams > 0) ? std::max(G, resident / s.E) : G;
+    return (KR + KL >= 12 || NT > kThreads) && *teams > 0 ? std::max(G, resident / s.E) : G;
   }
   const int64_t T = std::min(s.E, resident / G);
   *teams = T;
@@ -1510,8 +1510,19 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
                      s.E);
 }
 
-// Tiers of blocks held per lane: (KR in VGPRs, KL in LDS) = (1,0), (4,0), (12,0), (20,8).  The
-// first tier that holds every tensor at once runs (more workgroups for smaller tensors).  A
+// Tiers of blocks held per lane: (KR in VGPRs, KL in LDS) = (1,0), (4,0), then 10 in VGPRs in
+// workgroups of 1024 threads (4 waves per SIMD, see kTeamWideKR; up to 2,621,440 blocks in
+// all), then (12,0) and (20,8) at 256 threads.  The first tier that holds every tensor at once
+// runs (more workgroups for smaller tensors).  Same-box A/B of the 1024-thread tier against
+// the tier that held the tensor before it: an 8192x4096 tensor (against (20,8)): 4/6-MSE
+// packed 28.4 against 33.4 us (then routed to two passes), rtn6 packed 21.8 against 25.6,
+// 4/6-MAE fake-quant 32.0 against 35.2, rtn6 fake-quant 31.0 against 33.6; 4096x4112 and
+// 2048x8192 (against (12,0)): 4/6-MSE packed 19.4 / 18.0 against 20.8 / 20.2 us, rtn6 packed
+// 15.0 / 14.4 against 19.0 / 18.4, 4/6-MAE fake-quant 21.9 / 19.9 against 23.3 / 22.5, rtn6
+// fake-quant 21.5 / 20.3 against 25.2 / 24.2; two 4096x4096 tensors equal.  Before (4,0) it
+// measured equal or up to 6 % slower on tensors of 0.26 M blocks and less.  (12,0) is left
+// for batches of many mid-size tensors whose workgroups the 1024-thread tier cannot all place.
+// A
 // batch that no tier holds at once runs in teams (kTeamSmallKR + 0, kTeamWideKR + 0 or
 // kTeamKR + kTeamKL per lane) when one tensor fits: teams at different tensors overlap loads
 // with arithmetic.  Returns the blocks held per lane (1, 4, 12, 28, or 10 / 20 for teams), or 0
@@ -1532,13 +1543,15 @@ int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uin
   }
   NVFP4_FUSED_TIER(1, 0, false, kThreads)
   NVFP4_FUSED_TIER(4, 0, false, kThreads)
+  NVFP4_FUSED_TIER(kTeamWideKR, 0, false, 1024)
   NVFP4_FUSED_TIER(12, 0, false, kThreads)
   // A single Four Over Six tensor into packed output that the tiers above do not hold takes
-  // the two-pass path: there the single read is not faster.  Its second phase (the two trials
-  // per block) cannot overlap the tensor's own loads, and costs what the second read costs
-  // (4096x14336: 50.2 against 50.5 us; 8192x4096: 34.3 against 34.0 us).  Fake-quant output,
-  // rtn6 and batches are faster read once (weight: 60.6 against 66.6 us fake-quant, 39.3
-  // against 50.5 us rtn6; three 4096x4096 tensors, 4/6 packed: 44.5 against 47.1 us).
+  // the two-pass path: in the (20,8) tier, at two waves per SIMD, the single read is not
+  // faster.  Its second phase (the two trials per block) cannot overlap the tensor's own loads,
+  // and costs what the second read costs (4096x14336: 50.2 against 50.5 us; 8192x4096, before
+  // the 1024-thread tier took it: 34.3 against 34.0 us).  Fake-quant output, rtn6 and batches
+  // are faster read once (weight: 60.6 against 66.6 us fake-quant, 39.3 against 50.5 us rtn6;
+  // three 4096x4096 tensors, 4/6 packed: 44.5 against 47.1 us).
   if (MODE == NVFP4_FOUR_OVER_SIX && !FQ && s.E == 1) return 0;
   NVFP4_FUSED_TIER(20, 8, false, kThreads)
   if (s.nblk < kTeamSmallBlocks) {

@@ -188,7 +188,8 @@ def test_diagnostics(nv, orc, shape, with_stats):
 
 
 # Single-read calls: every tier of blocks held per lane, and every team tier.
-FUSED = [((256, 256), 1), ((1024, 4112), None), ((4096, 4112), None), ((4096, 14336), 28),
+FUSED = [((256, 256), 1), ((1024, 4112), None), ((4096, 4112), 10), ((8192, 4096), 10),
+         ((100, 328, 1024), None), ((4096, 14336), 28),
          ((40, 256, 256), None), ((600, 256, 256), 10), ((6, 1024, 16384), 20),
          ((10, 1024, 8192), 20), ((3, 4096, 4096), None)]
 
