@@ -244,16 +244,14 @@ nvfp4_status nvfp4_quantize_fused_noalloc(const uint16_t* in, int64_t E, int64_t
                                           hipStream_t stream);
 
 /* For a fused call of this shape, mode, rule and output form on the current device: the
- * most blocks a lane holds on chip (1, 4, 12, 10 in workgroups of 1024 threads, or 28; a
- * tensor spread over more workgroups leaves each lane fewer) if it reads its input once, 0 if
- * it takes the two-pass path, or minus a status code for bad arguments.  On MI355X up to
- * 3,670,016 blocks per launch (E * rows * cols / 16; 117 MB of bf16) are held at once.  A larger
- * batch whose single tensors fit (up to 2,621,440 blocks each) is read once too, by teams of
- * workgroups that take its tensors in turn: the call then returns 20, or 10 for tensors under
- * 262,144 blocks and for Four Over Six into packed output.  A single Four Over Six tensor into
- * packed output (E = 1) is read once only up to the 1024-thread tier (2,621,440 blocks); larger
- * ones take the two-pass path, which measured as fast for them (a 4096x14336 tensor: 50.5 us
- * two-pass, 50.2 us read once in the 28-block tier). */
+ * most blocks a lane holds on chip (1, 4 or 12 in workgroups of 256 threads, 10 or 14 in
+ * workgroups of 1024 threads, or 28; a tensor spread over more workgroups leaves each lane
+ * fewer) if it reads its input once, 0 if it takes the two-pass path, or minus a status code
+ * for bad arguments.  On MI355X up to 3,670,016 blocks per launch (E * rows * cols / 16; 117 MB
+ * of bf16) are held at once, in every mode.  A larger batch whose single tensors fit (up to
+ * 2,621,440 blocks each) is read once too, by teams of workgroups that take its tensors in
+ * turn: the call then returns 20, or 10 for tensors under 262,144 blocks and for Four Over Six
+ * into packed output. */
 int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols, nvfp4_mode mode,
                             nvfp4_rule rule, int fakequant);
 

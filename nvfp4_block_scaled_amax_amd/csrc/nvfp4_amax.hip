@@ -963,7 +963,13 @@ __device__ __forceinline__ void fused_tensor(
   uint8_t* scalesT = scales + base;
   char* outT = reinterpret_cast<char*>(out + 2 * base);
 
-  // phase 1: load every held block (all loads in flight together), magnitude max
+  // phase 1: load every held block (all loads in flight together), magnitude max.  In
+  // 1024-thread workgroups the blocks held in LDS are loaded straight into it
+  // (global_load_lds_dwordx4: each wave writes 1 KB, 16 bytes per lane in lane order, which is
+  // the layout of held[k][half][tid]), so they take no VGPRs on the way; lanes past the end
+  // load the last block again, which leaves the magnitude max as it is.  Each wave then reads
+  // back only its own lanes' blocks, after its own loads have landed.
+  constexpr bool kDma = NT == 1024 && KL > 0;
   uint4 r0[KR], r1[KR], l0[KL > 0 ? KL : 1], l1[KL > 0 ? KL : 1];
 #pragma unroll
   for (int k = 0; k < KR; ++k) {
@@ -977,20 +983,31 @@ __device__ __forceinline__ void fused_tensor(
 #pragma unroll
   for (int k = 0; k < KL; ++k) {
     const uint32_t u = ((uint32_t)(KR + k) * G + g) * NT + tid;
-    l0[k] = l1[k] = make_uint4(0u, 0u, 0u, 0u);
-    if (u < n) {
-      l0[k] = *reinterpret_cast<const uint4*>(inT + (u << 5));
-      l1[k] = *reinterpret_cast<const uint4*>(inT + (u << 5) + 16);
+    if constexpr (kDma) {
+      const uint4* src = reinterpret_cast<const uint4*>(inT + (min(u, n - 1) << 5));
+      __builtin_amdgcn_global_load_lds(src, &held[k][0][tid & ~63u], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + 1, &held[k][1][tid & ~63u], 16, 0, 0);
+    } else {
+      l0[k] = l1[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (u < n) {
+        l0[k] = *reinterpret_cast<const uint4*>(inT + (u << 5));
+        l1[k] = *reinterpret_cast<const uint4*>(inT + (u << 5) + 16);
+      }
     }
   }
   uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < KR; ++k) m = mag_max8(mag_max8(m, r0[k]), r1[k]);
+  if constexpr (kDma) __builtin_amdgcn_s_waitcnt(0);   // this wave's loads have landed
 #pragma unroll
   for (int k = 0; k < KL; ++k) {
-    m = mag_max8(mag_max8(m, l0[k]), l1[k]);
-    held[k][0][tid] = l0[k];
-    held[k][1][tid] = l1[k];
+    if constexpr (kDma) {
+      m = mag_max8(mag_max8(m, held[k][0][tid]), held[k][1][tid]);
+    } else {
+      m = mag_max8(mag_max8(m, l0[k]), l1[k]);
+      held[k][0][tid] = l0[k];
+      held[k][1][tid] = l1[k];
+    }
   }
   m = max(m & 0xFFFFu, m >> 16) << 16;
   m = wave_max_u32(m);
@@ -1510,24 +1527,24 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
                      s.E);
 }
 
-// Tiers of blocks held per lane: (KR in VGPRs, KL in LDS) = (1,0), (4,0), then 10 in VGPRs in
-// workgroups of 1024 threads (4 waves per SIMD, see kTeamWideKR; up to 2,621,440 blocks in
-// all), then (12,0) and (20,8) at 256 threads.  The first tier that holds every tensor at once
-// runs (more workgroups for smaller tensors).  Same-box A/B of the 1024-thread tier against
-// the tier that held the tensor before it: an 8192x4096 tensor (against (20,8)): 4/6-MSE
-// packed 28.4 against 33.4 us (then routed to two passes), rtn6 packed 21.8 against 25.6,
-// 4/6-MAE fake-quant 32.0 against 35.2, rtn6 fake-quant 31.0 against 33.6; 4096x4112 and
-// 2048x8192 (against (12,0)): 4/6-MSE packed 19.4 / 18.0 against 20.8 / 20.2 us, rtn6 packed
-// 15.0 / 14.4 against 19.0 / 18.4, 4/6-MAE fake-quant 21.9 / 19.9 against 23.3 / 22.5, rtn6
-// fake-quant 21.5 / 20.3 against 25.2 / 24.2; two 4096x4096 tensors equal.  Before (4,0) it
-// measured equal or up to 6 % slower on tensors of 0.26 M blocks and less.  (12,0) is left
-// for batches of many mid-size tensors whose workgroups the 1024-thread tier cannot all place.
-// A
-// batch that no tier holds at once runs in teams (kTeamSmallKR + 0, kTeamWideKR + 0 or
-// kTeamKR + kTeamKL per lane) when one tensor fits: teams at different tensors overlap loads
-// with arithmetic.  Returns the blocks held per lane (1, 4, 12, 28, or 10 / 20 for teams), or 0
-// for the two-pass path: when not even one tensor fits, and for a single Four Over Six tensor
-// into packed output beyond the 12-block tier (see below).
+// Tiers of blocks held per lane, (KR in VGPRs, KL in LDS) in workgroups of NT threads, tried in
+// this order: (1,0) and (4,0) at 256; (10,0) at 1024 (4 waves per SIMD, see kTeamWideKR; up
+// to 2,621,440 blocks in all); (12,0) at 256; (10,4) at 1024 (3,670,016 blocks); (20,8) at 256
+// (as many, at two waves per SIMD; Four Over Six fake-quant, which does not fit (10,4) in 128
+// VGPRs).  The first tier that holds every tensor at once runs (more workgroups for smaller
+// tensors).  Same-box A/B of the (10,0) tier against the tier that held the tensor before it:
+// an 8192x4096 tensor (against (20,8)): 4/6-MSE packed 28.4 against 33.4 us (then routed to
+// two passes), rtn6 packed 21.8 against 25.6, 4/6-MAE fake-quant 32.0 against 35.2, rtn6
+// fake-quant 31.0 against 33.6; 4096x4112 and 2048x8192 (against (12,0)): 4/6-MSE packed 19.4
+// / 18.0 against 20.8 / 20.2 us, rtn6 packed 15.0 / 14.4 against 19.0 / 18.4, 4/6-MAE
+// fake-quant 21.9 / 19.9 against 23.3 / 22.5, rtn6 fake-quant 21.5 / 20.3 against 25.2 / 24.2;
+// two 4096x4096 tensors equal.  Before (4,0) it measured equal or up to 6 % slower on tensors
+// of 0.26 M blocks and less.  (12,0) is left for batches of many mid-size tensors whose
+// workgroups the 1024-thread tier cannot all place.  A batch that no tier holds at once runs in
+// teams (kTeamSmallKR + 0, kTeamWideKR + 0 or kTeamKR + kTeamKL per lane) when one tensor
+// fits: teams at different tensors overlap loads with arithmetic.  Returns the blocks held per
+// lane (1, 4, 10, 12, 14 or 28, or 10 / 20 for teams), or 0 for the two-pass path, when not
+// even one tensor fits.
 template <int MODE, int RULE, bool FQ>
 int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uint8_t* codes,
                uint8_t* scales, uint16_t* out, float* alpha, hipStream_t stream) {
@@ -1545,14 +1562,15 @@ int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uin
   NVFP4_FUSED_TIER(4, 0, false, kThreads)
   NVFP4_FUSED_TIER(kTeamWideKR, 0, false, 1024)
   NVFP4_FUSED_TIER(12, 0, false, kThreads)
-  // A single Four Over Six tensor into packed output that the tiers above do not hold takes
-  // the two-pass path: in the (20,8) tier, at two waves per SIMD, the single read is not
-  // faster.  Its second phase (the two trials per block) cannot overlap the tensor's own loads,
-  // and costs what the second read costs (4096x14336: 50.2 against 50.5 us; 8192x4096, before
-  // the 1024-thread tier took it: 34.3 against 34.0 us).  Fake-quant output, rtn6 and batches
-  // are faster read once (weight: 60.6 against 66.6 us fake-quant, 39.3 against 50.5 us rtn6;
-  // three 4096x4096 tensors, 4/6 packed: 44.5 against 47.1 us).
-  if (MODE == NVFP4_FOUR_OVER_SIX && !FQ && s.E == 1) return 0;
+  // 10 in VGPRs and 4 in LDS in 1024-thread workgroups (one per CU, 3,670,016 blocks in all: the
+  // 4096x14336 weight), before (20,8), which holds as many at two waves per SIMD.  Same-box A/B
+  // on the weight: 4/6-MSE packed 44.6 against 50.7 us (then routed to two passes: (20,8) read
+  // once was no faster than two passes, 50.2 against 50.5 us), rtn6 packed 33.1 against 38.6,
+  // rtn6 fake-quant 53.2 against 55.8; three 4096x4096 tensors 4/6 packed 39.9 against 40.7.
+  // Four Over Six fake-quant needs more than 128 VGPRs here and keeps (20,8).
+  if constexpr (!(MODE == NVFP4_FOUR_OVER_SIX && FQ)) {
+    NVFP4_FUSED_TIER(kTeamWideKR, 4, false, 1024)
+  }
   NVFP4_FUSED_TIER(20, 8, false, kThreads)
   if (s.nblk < kTeamSmallBlocks) {
     NVFP4_FUSED_TIER(kTeamSmallKR, 0, true, kThreads)

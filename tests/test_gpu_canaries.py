@@ -189,7 +189,7 @@ def test_diagnostics(nv, orc, shape, with_stats):
 
 # Single-read calls: every tier of blocks held per lane, and every team tier.
 FUSED = [((256, 256), 1), ((1024, 4112), None), ((4096, 4112), 10), ((8192, 4096), 10),
-         ((100, 328, 1024), None), ((4096, 14336), 28),
+         ((100, 328, 1024), None), ((4096, 14336), 14),
          ((40, 256, 256), None), ((600, 256, 256), 10), ((6, 1024, 16384), 20),
          ((10, 1024, 8192), 20), ((3, 4096, 4096), None)]
 
@@ -200,13 +200,11 @@ FUSED = [((256, 256), 1), ((1024, 4112), None), ((4096, 4112), 10), ((8192, 4096
 def test_fused(nv, orc, shape, tier, mode, rule, fq):
     got_tier = nv.fused_blocks_per_lane(shape, mode, rule, fq)
     say("[canary-fused] %s %s fq=%s: %d blocks per lane" % (shape, mode, fq, got_tier))
-    if shape == (4096, 14336) and not fq and mode == "four_over_six":
-        tier = 0                            # routed to the two-pass path
     if tier == 20 and not fq and mode == "four_over_six":
         tier = 10                           # the wide-workgroup team tiers (1024 / 512 threads)
     if tier is not None:
         assert got_tier == tier
-    assert got_tier > 0 or tier == 0
+    assert got_tier > 0
     x = W.bits(W.generate("moe" if len(shape) == 3 else "weight", shape))
     E = shape[0] if len(shape) == 3 else 1
     xg = Guarded(shape, torch.bfloat16, init=bits_gpu(x))

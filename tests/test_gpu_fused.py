@@ -2,8 +2,8 @@
 
 The fused entry points must give the dynamic entry points' results bit for bit: codes, scale
 bytes, alpha bits and fake-quant bf16 bits equal to the oracle's.  Covered here: every tier of
-blocks held per lane (1, 4, 12, 10 in 1024-thread workgroups and 28, confirmed through the shape
-query), the batched form,
+blocks held per lane (1, 4 and 12 in 256-thread workgroups, 10 and 10 + 4 in 1024-thread ones, 28,
+confirmed through the shape query), the batched form,
 batches run in teams (10 or 20 per lane, in workgroups of 256, 512 or 1024 threads; the 64-expert
 MoE batch whole),
 the edge tensors, poisoning, the bounded grid-wide wait forced from the host (every workgroup
@@ -90,7 +90,7 @@ def test_fused_random_shapes(nv, orc):
 
 # Shapes that select each tier on a 256-CU MI355X (the test checks the tier it gets).
 TIERS = [(1, (256, 256)), (4, (1024, 4112)), (10, (4096, 4112)), (10, (8192, 4096)),
-         (12, (100, 328, 1024)), (28, (4096, 14336))]
+         (12, (100, 328, 1024)), (14, (4096, 14336))]
 
 
 @pytest.mark.parametrize("tier,shape", TIERS, ids=["tier%d-%s" % (t, "x".join(map(str, s)))
@@ -102,14 +102,12 @@ TIERS = [(1, (256, 256)), (4, (1024, 4112)), (10, (4096, 4112)), (10, (8192, 409
 def test_fused_tiers_whole_tensor(nv, orc, tier, shape, mode, rule, fq):
     got_tier = nv.fused_blocks_per_lane(shape, mode, rule, fq)
     say("[fused] %s %s/%s fq=%s: %d blocks per lane" % (shape, mode, rule, fq, got_tier))
-    if mode == "four_over_six" and not fq and tier == 28:
-        assert got_tier == 0            # a single 4/6 packed tensor this large: two-pass
-    else:
-        if tier == 28 and got_tier == 0:
-            pytest.fail("the weight-sized tensor does not fit on chip on this device")
-        assert got_tier >= 1
-        if tier in (1, 10, 28) or (tier == 12 and not fq):
-            assert got_tier == tier, got_tier
+    want = 28 if (tier == 14 and mode == "four_over_six" and fq) else tier   # 4/6 fq: (20,8)
+    if tier == 14 and got_tier == 0:
+        pytest.fail("the weight-sized tensor does not fit on chip on this device")
+    assert got_tier >= 1
+    if tier in (1, 10, 14) or (tier == 12 and not fq):
+        assert got_tier == want, got_tier
     x = W.bits(W.weight(shape, seed=300 + tier))
     assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq,
                           "tier%d" % tier)
@@ -119,7 +117,7 @@ def test_fused_tiers_are_all_exercised(nv):
     seen = {nv.fused_blocks_per_lane(s, m, r, f) for _, s in TIERS
             for (m, r, f) in (("four_over_six", "mse", False), ("rtn6", "mse", True),
                               ("four_over_six", "mae", True))}
-    assert {1, 4, 10, 12, 28} <= seen, seen
+    assert {1, 4, 10, 12, 14, 28} <= seen, seen
 
 
 @pytest.mark.parametrize("name", sorted(EDGE))
@@ -212,24 +210,22 @@ def test_fused_teams_moe_full_size(nv, orc):
 
 
 def test_fused_two_pass_route(nv, orc):
-    """A tensor too large to hold on chip, a single Four Over Six tensor into packed output
-    beyond the 12-block tier, and in-place fake-quant take the two-pass path."""
+    """A tensor too large to hold on chip and in-place fake-quant take the two-pass path; every
+    tensor up to 3,670,016 blocks is read once, in every mode (a single Four Over Six tensor
+    into packed output too, in the 1024-thread tiers)."""
     shape = (4096, 16384)                                  # 4.2 M blocks
     assert nv.fused_blocks_per_lane(shape, "four_over_six", "mse", False) == 0
     assert nv.fused_blocks_per_lane(shape, "rtn6", "mse", False) == 0
-    # a single 4/6 tensor into packed output: read once in the 1024-thread tier up to
-    # 2,621,440 blocks (8192x4096), routed to two passes beyond it (4096x14336)
     assert nv.fused_blocks_per_lane((8192, 4096), "four_over_six", "mae", False) == 10
+    assert nv.fused_blocks_per_lane((4096, 14336), "four_over_six", "mae", False) == 14
     for shp in ((4096, 14336), (8192, 4096)):
-        if shp == (4096, 14336):                          # would fit, routed to two passes
-            assert nv.fused_blocks_per_lane(shp, "four_over_six", "mae", False) == 0
         assert nv.fused_blocks_per_lane(shp, "rtn6", "mse", False) > 0
         assert nv.fused_blocks_per_lane(shp, "four_over_six", "mae", True) > 0
         assert nv.fused_blocks_per_lane((2,) + shp[:1] + (shp[1] // 2,), "four_over_six",
-                                        "mse", False) > 0    # batches still read once
-    xr = W.bits(W.weight((8192, 4096), seed=501))
+                                        "mse", False) > 0    # batches read once
+    xr = W.bits(W.weight((4096, 14336), seed=501))
     got = run_fused(nv, xr, "four_over_six", "maxerr", False)
-    assert_matches_oracle(orc, xr, got, "four_over_six", "maxerr", False, "routed")
+    assert_matches_oracle(orc, xr, got, "four_over_six", "maxerr", False, "weight-read-once")
     x = W.bits(W.weight(shape, seed=500))
     got = run_fused(nv, x, "four_over_six", "mse", False)
     assert_matches_oracle(orc, x, got, "four_over_six", "mse", False, "too-large")

@@ -52,7 +52,7 @@ def _call(L, fn, x, E, rows, cols, mode, rule, outs, *extra):
 # (shape, mode, rule): consecutive calls, each smaller than the one before it
 SEQUENCES = [
     [((6, 1024, 16384), 1, 0), ((3, 256, 4096), 1, 1)],        # teams of 10, then all at once
-    [((4096, 14336), 1, 0), ((256, 256), 0, 0)],               # 28 per lane, then 1 per lane
+    [((4096, 14336), 1, 0), ((256, 256), 0, 0)],               # 10 + 4 per lane, then 1 per lane
     [((600, 256, 256), 1, 2), ((40, 128, 512), 1, 0)],          # teams of 10, then smaller
     [((4096, 16384), 1, 0), ((1024, 4112), 1, 0)],              # two-pass route, then tier 4
 ]
