@@ -250,8 +250,8 @@ nvfp4_status nvfp4_quantize_fused_noalloc(const uint16_t* in, int64_t E, int64_t
  * for bad arguments.  On MI355X up to 3,670,016 blocks per launch (E * rows * cols / 16; 117 MB
  * of bf16) are held at once, in every mode.  A larger batch whose single tensors fit (up to
  * 2,621,440 blocks each) is read once too, by teams of workgroups that take its tensors in
- * turn: the call then returns 20, or 10 for tensors under 262,144 blocks and for Four Over Six
- * into packed output. */
+ * turn: the call then returns 20, or 10 for tensors under 262,144 blocks, or 10 or 13 for
+ * Four Over Six into packed output. */
 int nvfp4_fused_single_read(int64_t E, int64_t rows, int64_t cols, nvfp4_mode mode,
                             nvfp4_rule rule, int fakequant);
 

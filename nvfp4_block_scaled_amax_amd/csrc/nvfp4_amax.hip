@@ -864,21 +864,24 @@ constexpr int64_t kFusedMaxTensorWGs = 512;           // see fused_tier_wgs
 constexpr int64_t kTeamSmallBlocks = INT64_C(1) << 18;
 constexpr int kTeamSmallKR = 10;
 // Four Over Six into packed output (from kTeamSmallBlocks on) runs its teams with wider
-// workgroups: kTeamWideKR blocks per lane in VGPRs, none in LDS, at most 128 VGPRs, so that a
-// workgroup of 512 threads puts 2 waves on each SIMD and two of them share a CU; or one of 1024
-// threads, 4 waves per SIMD, one per CU.  The block pass of a held tensor needs about four
-// waves per SIMD to keep the VALU issuing (two per SIMD issue about half as fast), and the two
-// workgroups that share a CU (workgroups i and i + #CUs) should compute at the same time,
-// which the odd/even start of the teams gives when there are at least four teams (teams y and
-// y + T/2 share CUs).  With fewer, the 1024-thread form keeps every CU in one team.  Same-box
-// A/B (4/6-MSE packed, us per call; 18 + 2 at 256 threads / 512 threads / 1024 threads):
-// 64x2048x5120 (4 teams) 418 / 389 / 405; 40x2048x6144 (3) 376 / 352 / 366; 24x3072x4096 (3)
-// 224 / 216 / 210; 96x1024x4096 (9) 279 / 273 / 274; 16x2048x8192 (2) 215 / 211 / 176;
-// 12x4096x4096 (2) 165 / 154 / 135.  rtn6 and fake-quant output keep the 18 + 2 tier: there
-// the wide tiers measured equal or slower (rtn6 on the MoE batch 352 / 353 / 384 us, rtn6
+// workgroups (at most 128 VGPRs): 512 threads, 2 waves on each SIMD and two workgroups per CU,
+// holding kTeamWideKR blocks per lane in VGPRs, or kTeamWideKR - 1 in VGPRs and 4 in LDS; or
+// 1024 threads, 4 waves per SIMD, one per CU, kTeamWideKR in VGPRs.  The block pass of a held
+// tensor needs about four waves per SIMD to keep the VALU issuing (two per SIMD issue about
+// half as fast), and the two workgroups that share a CU (workgroups i and i + #CUs) should
+// compute at the same time: with teams of a power-of-two size and at least four teams, the
+// odd/even start of the teams gives that (teams y and y + T/2 share CUs); otherwise the
+// 1024-thread form keeps every CU in one team.  Same-box A/B (4/6-MSE packed, us per call; 18 +
+// 2 at 256 threads / 10 at 512 threads, teams widened to fill every slot / 10 at 1024
+// threads): 64x2048x5120 (4 teams of 128 at 512) 418 / 389 / 405; 40x2048x6144 (3 teams of
+// 170) 376 / 352 / 366; 24x3072x4096 (3) 224 / 216 / 210; 96x1024x4096 (9 of 56) 279 / 273 /
+// 274; 16x2048x8192 (2) 215 / 211 / 176; 12x4096x4096 (2) 165 / 154 / 135.  Then with
+// power-of-two teams, 9 + 4 when 10 alone cannot make four of them: 40x2048x6144 293 against
+// 349 us, 24x3072x4096 179 against 213 (4 teams of 128, 9 + 4), 96x1024x4096 263 against 265
+// (8 of 64), the others unchanged.  rtn6 and fake-quant output keep the 18 + 2 tier: there the
+// wide tiers measured equal or slower (rtn6 on the MoE batch 352 / 353 / 384 us, rtn6
 // fake-quant 518 / 561 / 528 us, 4/6-MAE fake-quant 547 / 556 / 586 us).
 constexpr int kTeamWideKR = 10;
-constexpr int64_t kTeamWideMinTeams = 3;
 constexpr int kFusedGroups = 16;
 constexpr int kLineWords = 32;                           // 128 bytes
 constexpr int64_t kFusedWsWords = (kFusedGroups + 1) * kLineWords;
@@ -964,12 +967,12 @@ __device__ __forceinline__ void fused_tensor(
   char* outT = reinterpret_cast<char*>(out + 2 * base);
 
   // phase 1: load every held block (all loads in flight together), magnitude max.  In
-  // 1024-thread workgroups the blocks held in LDS are loaded straight into it
+  // workgroups of 512 and 1024 threads the blocks held in LDS are loaded straight into it
   // (global_load_lds_dwordx4: each wave writes 1 KB, 16 bytes per lane in lane order, which is
   // the layout of held[k][half][tid]), so they take no VGPRs on the way; lanes past the end
   // load the last block again, which leaves the magnitude max as it is.  Each wave then reads
   // back only its own lanes' blocks, after its own loads have landed.
-  constexpr bool kDma = NT == 1024 && KL > 0;
+  constexpr bool kDma = NT >= 512 && KL > 0;
   uint4 r0[KR], r1[KR], l0[KL > 0 ? KL : 1], l1[KL > 0 ? KL : 1];
 #pragma unroll
   for (int k = 0; k < KR; ++k) {
@@ -1527,6 +1530,27 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
                      s.E);
 }
 
+// Four Over Six teams in 512-thread workgroups, KR + KL blocks per lane (the KL in LDS, loaded
+// straight into it), in teams of a power-of-two number of workgroups: then the two workgroups
+// that share a CU (i and i + #CUs) belong to teams y and y + T/2, which the odd/even start
+// puts in the same phase.  Taken when at least four such teams fit; returns whether it was
+// (and launches when asked).
+template <int MODE, int RULE, bool FQ, int KR, int KL>
+bool fused_team512(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws,
+                   uint8_t* codes, uint8_t* scales, float* alpha, hipStream_t stream) {
+  constexpr int64_t per_wg = (int64_t)(KR + KL) * 512;
+  const int64_t G = (s.nblk + per_wg - 1) / per_wg;
+  int64_t Gp = 1;
+  while (Gp < G) Gp <<= 1;
+  const int64_t resident = fused_resident_wgs<MODE, RULE, FQ, KR, KL, true, 512>();
+  const int64_t T = std::min(s.E, resident / Gp);
+  if (resident < 4 * Gp || T < 4) return false;
+  if (launch)
+    fused_launch<MODE, RULE, FQ, KR, KL, true, 512>(Gp, T, in, s, ws, codes, scales, nullptr,
+                                                    alpha, stream);
+  return true;
+}
+
 // Tiers of blocks held per lane, (KR in VGPRs, KL in LDS) in workgroups of NT threads, tried in
 // this order: (1,0) and (4,0) at 256; (10,0) at 1024 (4 waves per SIMD, see kTeamWideKR; up
 // to 2,621,440 blocks in all); (12,0) at 256; (10,4) at 1024 (3,670,016 blocks); (20,8) at 256
@@ -1543,8 +1567,8 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
 // workgroups the 1024-thread tier cannot all place.  A batch that no tier holds at once runs in
 // teams (kTeamSmallKR + 0, kTeamWideKR + 0 or kTeamKR + kTeamKL per lane) when one tensor
 // fits: teams at different tensors overlap loads with arithmetic.  Returns the blocks held per
-// lane (1, 4, 10, 12, 14 or 28, or 10 / 20 for teams), or 0 for the two-pass path, when not
-// even one tensor fits.
+// lane (1, 4, 10, 12, 14 or 28, or 10 / 13 / 20 for teams), or 0 for the two-pass path, when
+// not even one tensor fits.
 template <int MODE, int RULE, bool FQ>
 int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uint8_t* codes,
                uint8_t* scales, uint16_t* out, float* alpha, hipStream_t stream) {
@@ -1576,12 +1600,13 @@ int fused_try(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws, uin
     NVFP4_FUSED_TIER(kTeamSmallKR, 0, true, kThreads)
   }
   if constexpr (MODE == NVFP4_FOUR_OVER_SIX && !FQ) {
-    // wide workgroups: 512 threads when that gives at least kTeamWideMinTeams teams, else 1024
-    int64_t T512 = 0;
-    fused_tier_wgs<MODE, RULE, FQ, kTeamWideKR, 0, true, 512>(s, &T512);
-    if (T512 >= kTeamWideMinTeams) {
-      NVFP4_FUSED_TIER(kTeamWideKR, 0, true, 512)
-    }
+    // wide workgroups: 512 threads in aligned teams of 10 or 9 + 4 per lane, else 1024
+    if (fused_team512<MODE, RULE, FQ, kTeamWideKR, 0>(launch, in, s, ws, codes, scales, alpha,
+                                                      stream))
+      return kTeamWideKR;
+    if (fused_team512<MODE, RULE, FQ, kTeamWideKR - 1, 4>(launch, in, s, ws, codes, scales,
+                                                          alpha, stream))
+      return kTeamWideKR + 3;
     NVFP4_FUSED_TIER(kTeamWideKR, 0, true, 1024)
   }
   NVFP4_FUSED_TIER(kTeamKR, kTeamKL, true, kThreads)

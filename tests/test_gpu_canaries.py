@@ -191,7 +191,7 @@ def test_diagnostics(nv, orc, shape, with_stats):
 FUSED = [((256, 256), 1), ((1024, 4112), None), ((4096, 4112), 10), ((8192, 4096), 10),
          ((100, 328, 1024), None), ((4096, 14336), 14),
          ((40, 256, 256), None), ((600, 256, 256), 10), ((6, 1024, 16384), 20),
-         ((10, 1024, 8192), 20), ((3, 4096, 4096), None)]
+         ((10, 1024, 8192), 20), ((6, 3072, 4096), None), ((3, 4096, 4096), None)]
 
 
 @pytest.mark.parametrize("shape,tier", FUSED, ids=[str(s) for s, _ in FUSED])

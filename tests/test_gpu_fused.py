@@ -157,11 +157,10 @@ def test_fused_bounded_wait_fallback(nv, orc, limit, shape):
 
 
 # Batches that no tier holds at once but whose single tensors fit: teams of workgroups take the
-# tensors in turn (odd teams start half a cycle late).  10 blocks per lane for tensors under
-# 262,144 blocks and for Four Over Six into packed output (in 512-thread workgroups when that
-# gives at least three teams, else 1024-thread ones), 20 otherwise.
+# tensors in turn (odd teams start half a cycle late); team_tier gives the blocks per lane.
 TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),     # 2 teams of 1024 threads
          ((10, 1024, 8192), "four_over_six", "mse", False),     # 4 teams of 512 threads
+         ((6, 3072, 4096), "four_over_six", "mae", False),      # 4 teams of 512, 9 + 4 per lane
          ((5, 1000, 14336), "four_over_six", "mae", True),
          ((12, 512, 14336), "rtn6", "mse", False),
          ((3, 2048, 14336), "four_over_six", "maxerr", False),
@@ -170,8 +169,21 @@ TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),     # 2 teams of 102
 
 
 def team_tier(shape, mode, fq):
-    small = shape[1] * shape[2] // 16 < 2 ** 18
-    return 10 if small or (mode == "four_over_six" and not fq) else 20
+    """Blocks per lane of the team tier a batch gets on a 256-CU MI355X: 10 for tensors under
+    262,144 blocks; for Four Over Six into packed output, 10 or 9 + 4 in 512-thread workgroups
+    when that makes at least four teams of a power-of-two size (512 resident workgroups), else
+    10 in 1024-thread ones; 20 otherwise."""
+    E, nblk = shape[0], shape[1] * shape[2] // 16
+    if nblk < 2 ** 18:
+        return 10
+    if mode != "four_over_six" or fq:
+        return 20
+    for per_lane in (10, 13):
+        g = -(-nblk // (per_lane * 512))
+        gp = 1 << (g - 1).bit_length()
+        if 4 * gp <= 512 and E >= 4:
+            return per_lane
+    return 10
 
 
 @pytest.mark.parametrize("shape,mode,rule,fq", TEAMS, ids=["t%d" % i for i in range(len(TEAMS))])
