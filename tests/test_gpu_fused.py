@@ -249,6 +249,37 @@ def test_fused_two_pass_route(nv, orc):
     assert np.array_equal(u16(y), ref["y"])
 
 
+def test_fused_two_streams_at_once(nv, orc):
+    """Two single-read calls enqueued together on two streams (default priority), each sized
+    to fill the chip: one may find the CUs held by the other, and the bounded wait keeps every
+    workgroup moving (a workgroup that gives up computes the tensor amax itself).  Three rounds;
+    every result equals the oracle's."""
+    xa = W.bits(W.weight((8192, 4096), seed=610))             # 1024-thread tier, whole chip
+    xb = W.bits(W.generate("moe", (10, 1024, 8192)))          # 4 teams of 512-thread workgroups
+    ga, gb = to_gpu(xa), to_gpu(xb)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for rnd in range(3):
+        say("[fused] two streams, round %d" % rnd)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sa):
+            ca, sca, aa = nv.quantize_fused(ga, "four_over_six", "mse")
+        with torch.cuda.stream(sb):
+            yb, ab = nv.fakequant_fused(gb, "four_over_six", "mae") if rnd % 2 else (None, None)
+            if yb is None:
+                cb, scb, ab = nv.quantize_fused(gb, "four_over_six", "mse")
+        torch.cuda.synchronize()
+        assert_matches_oracle(orc, xa, dict(codes=ca.cpu().numpy(), scales=sca.cpu().numpy(),
+                                            alpha=aa.cpu().numpy()),
+                              "four_over_six", "mse", False, "stream a %d" % rnd)
+        if rnd % 2:
+            assert_matches_oracle(orc, xb, dict(y=u16(yb), alpha=ab.cpu().numpy()),
+                                  "four_over_six", "mae", True, "stream b %d" % rnd)
+        else:
+            assert_matches_oracle(orc, xb, dict(codes=cb.cpu().numpy(), scales=scb.cpu().numpy(),
+                                                alpha=ab.cpu().numpy()),
+                                  "four_over_six", "mse", False, "stream b %d" % rnd)
+
+
 def test_fused_workspace_content_and_reuse(nv, orc):
     """The workspace may hold anything before a call; one workspace serves consecutive calls
     on a stream, and a larger one than needed is fine."""
