@@ -20,8 +20,9 @@
 //   fused_kernel     single-read dynamic quantization for tensors that fit on chip: loads
 //                    and keeps each lane's blocks (VGPRs + LDS), reduces amax, waits for
 //                    every workgroup of the tensor at a grid-wide counter, then runs the
-//                    block pass on the blocks it holds; a batch larger than the chip runs as
-//                    teams of workgroups that take its tensors in turn
+//                    block pass on the blocks it holds; workgroups of 256, 512 or 1024
+//                    threads by tier; a batch larger than the chip runs as teams of
+//                    workgroups that take its tensors in turn
 //   dequant_kernel   packed codes + scale bytes + alpha -> bf16, one block per lane
 //
 // All floating-point steps of the encoding are IEEE binary32 with round-to-nearest-even, no
@@ -806,8 +807,9 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 // ----------------------------------------------------------------------------- fused path
 // Single-read dynamic quantization.  alpha depends on the whole tensor, so the two-pass path
 // reads the input twice (amax pass, block pass).  Here each lane keeps its blocks on chip
-// between the two phases: KR blocks in VGPRs and KL in LDS, blocks (k*G + g)*256 + lane for
-// k < KR + KL (coalesced per k).  Phase 1 loads them and reduces the magnitude max.  The
+// between the two phases: KR blocks in VGPRs and KL in LDS, blocks (k*G + g)*NT + lane for
+// k < KR + KL (coalesced per k; NT threads per workgroup).  Phase 1 loads them and reduces the
+// magnitude max.  The
 // workgroups of a tensor then meet at a two-level counter in the caller's workspace; the last
 // to arrive publishes amax, and each workgroup runs the block pass on the blocks it holds.
 // The host sizes the grid so that every workgroup can be resident at once.  The wait is
