@@ -165,7 +165,9 @@ TEAMS = [((6, 1024, 16384), "four_over_six", "mse", False),     # 2 teams of 102
          ((12, 512, 14336), "rtn6", "mse", False),
          ((3, 2048, 14336), "four_over_six", "maxerr", False),
          ((600, 256, 256), "four_over_six", "mse", False),     # one-workgroup teams
-         ((700, 128, 512), "four_over_six", "mae", True)]
+         ((700, 128, 512), "four_over_six", "mae", True),
+         ((16, 1024, 4096), "rtn6", "mse", False),              # teams of 52 rounded to 64
+         ((16, 1024, 4096), "four_over_six", "mae", True)]
 
 
 def team_tier(shape, mode, fq):
