@@ -19,7 +19,8 @@
 //   workspace, and the last to arrive sums the slots in a fixed order)
 //   fused_kernel     single-read dynamic quantization for tensors that fit on chip: loads
 //                    and keeps each lane's blocks (VGPRs + LDS), reduces amax, waits for
-//                    every workgroup of the tensor at a grid-wide counter, then runs the
+//                    every workgroup of the tensor (per-workgroup slots read by one
+//                    collector, or a two-level counter), then runs the
 //                    block pass on the blocks it holds; workgroups of 256, 512 or 1024
 //                    threads by tier; a batch larger than the chip runs as teams of
 //                    workgroups that take its tensors in turn
@@ -810,8 +811,8 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 // between the two phases: KR blocks in VGPRs and KL in LDS, blocks (k*G + g)*NT + lane for
 // k < KR + KL (coalesced per k; NT threads per workgroup).  Phase 1 loads them and reduces the
 // magnitude max.  The
-// workgroups of a tensor then meet at a two-level counter in the caller's workspace; the last
-// to arrive publishes amax, and each workgroup runs the block pass on the blocks it holds.
+// workgroups of a tensor then meet in the caller's workspace (see wait_collector and
+// wait_groups), amax is published, and each workgroup runs the block pass on the blocks it holds.
 // The host sizes the grid so that every workgroup can be resident at once.  The wait is
 // bounded: after `wait_polls` polls or `wait_ticks` ticks of the device's constant-rate wall
 // clock, whichever comes first, a workgroup computes the tensor amax itself from the input (the
@@ -819,7 +820,9 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
 // bound from the work (a small multiple of the launch's expected load time), so that a
 // workgroup kept waiting by CUs held elsewhere gives up after a few hundred microseconds.
 //
-// Workspace of one tensor (kFusedWsWords words, zeroed before the launch), one 128-byte line
+// Workspace of one tensor (kFusedWsWords words, zeroed before the launch).  The collector form
+// of the wait keeps one 16-bit slot per workgroup in lines 0-7 and the published amax at the
+// start of lines 8-15.  The group form keeps one 128-byte line
 // per group so that arrivals and polls spread over many lines.  Workgroup g belongs to group
 // g % S, with S = min(16, max(1, G / 8)) groups of at least 8 workgroups (one group for up to
 // 16 workgroups).  Line i starts with one 64-bit word that holds the group's max in its low
@@ -887,6 +890,12 @@ constexpr int kTeamWideKR = 10;
 constexpr int kFusedGroups = 16;
 constexpr int kLineWords = 32;                           // 128 bytes
 constexpr int64_t kFusedWsWords = (kFusedGroups + 1) * kLineWords;
+// The collector form of the wait (see wait_collector): 16-bit slots in lines 0-7, flags at the
+// start of lines 8-15.
+constexpr uint32_t kFlagLine0 = 8, kFlagLines = 8;
+static_assert(2 * kFusedMaxTensorWGs <= 4 * kLineWords * kFlagLine0 &&
+                  (kFlagLine0 + kFlagLines) * kLineWords <= kFusedWsWords,
+              "fused workspace: one slot per workgroup and the flag lines");
 static_assert(kFusedWsWords == NVFP4_FUSED_WS_WORDS, "workspace size of the fused calls");
 
 // Magnitude max of tensor t computed by one workgroup of NT threads alone (the fallback of the
@@ -950,10 +959,136 @@ __device__ __forceinline__ void fused_poison(uint32_t u, char* codesT, uint8_t* 
   }
 }
 
+// The grid-wide wait of the G workgroups of one tensor, in one of two forms, each bounded by
+// polls and wall-clock ticks.  Both return the tensor's magnitude max (bf16 magnitude bits
+// << 16) in lane 0, or 0xFFFFFFFF when the wait gave up ("compute it here").  wt is the tensor's
+// workspace (kFusedWsWords words, zero at the call's start), wgm this workgroup's max.
+//
+// Collector form (wave 0 of every workgroup).  Each workgroup stores its max with a set top
+// bit into its own 16-bit slot (words 0-255: up to 512 slots): the value is its own flag, so
+// nothing orders one word against another.  Workgroup 0 alone reads all slots (16 bytes per
+// lane) until each is set, then writes max | 1 to kFlagLines flag lines, each of which a
+// share of the workgroups polls.  From the last arrival to the release this is a store, one
+// read of the slots and a store, about half the chain of the group form.
+// Two words at device scope (the coherence of agent-scope atomic loads) from a uniform base
+// plus a lane's byte offset (plus 512 bytes when HI), waited for in the same statement.
+template <bool HI>
+__device__ __forceinline__ uint2 load_slots(const uint32_t* base, uint32_t off) {
+  uint2 v;
+  if (HI)
+    asm volatile("global_load_dwordx2 %0, %1, %2 offset:512 sc1\n\ts_waitcnt vmcnt(0)"
+                 : "=&v"(v) : "v"(off), "s"(base) : "memory");
+  else
+    asm volatile("global_load_dwordx2 %0, %1, %2 sc1\n\ts_waitcnt vmcnt(0)"
+                 : "=&v"(v) : "v"(off), "s"(base) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ void slots_check(uint2 v, uint32_t first, uint32_t G, bool& ok,
+                                            uint32_t& mx) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (first + c < G) {
+      const uint32_t h = ((c < 2 ? v.x : v.y) >> (16 * (c & 1))) & 0xFFFFu;
+      ok = ok && (h & 0x8000u);
+      mx = max(mx, h & 0x7FFFu);
+    }
+}
+
+__device__ __forceinline__ uint32_t wait_collector(uint32_t* wt, uint32_t wgm, uint32_t g,
+                                                   uint32_t G, uint32_t lane,
+                                                   uint32_t wait_polls, uint64_t wait_ticks) {
+  if (lane == 0)
+    __hip_atomic_store(reinterpret_cast<uint16_t*>(wt) + g, (uint16_t)(0x8000u | (wgm >> 16)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t t0 = wall_clock64();
+  if (g == 0) {
+    uint32_t polls = 0, mx = 0;
+    bool done = false;
+    for (;;) {                                     // lane l reads slots 4l.. and 256 + 4l..
+      bool ok = true;
+      mx = 0;
+      if (4 * lane < G) slots_check(load_slots<false>(wt, 8 * lane), 4 * lane, G, ok, mx);
+      if (256 + 4 * lane < G) slots_check(load_slots<true>(wt, 8 * lane), 256 + 4 * lane, G, ok, mx);
+      if (__all(ok)) { done = true; break; }
+      if (polls++ >= wait_polls || wall_clock64() - t0 > wait_ticks) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (done) {
+      mx = wave_max_u32(mx);
+      if (lane < kFlagLines)
+        __hip_atomic_store(wt + (kFlagLine0 + lane) * kLineWords, (mx << 16) | 1u,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  uint32_t flag = 0;
+  if (lane == 0) {
+    const uint32_t* line = wt + (kFlagLine0 + g % kFlagLines) * kLineWords;
+    uint32_t polls = 0;
+    while (!((flag = __hip_atomic_load(line, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & 1u)) {
+      if (polls++ >= wait_polls || wall_clock64() - t0 > wait_ticks) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  return (flag & 1u) ? (flag & ~1u) : 0xFFFFFFFFu;
+}
+
+// Group form (lane 0).  Groups of at least 8 workgroups, at most 16 groups, one 128-byte line
+// each; one group needs no top level.  Up to 16 workgroups meet on one line (measured 11 %
+// faster for the 16-workgroup 256x256 call); 128 workgroups on one line measured 1.5x slower
+// than 16 groups of 8.  A line starts with one 64-bit word: the max in its low half and the
+// arrival count in its high half; word 2 is the group's ready flag.
+__device__ __forceinline__ uint32_t wait_groups(uint32_t* wt, uint32_t wgm, uint32_t g,
+                                                uint32_t G, uint32_t lane,
+                                                uint32_t wait_polls, uint64_t wait_ticks) {
+  if (lane != 0) return 0xFFFFFFFFu;
+  const uint32_t S = G <= 16u ? 1u : min((uint32_t)kFusedGroups, max(1u, G / 8u));
+  const uint32_t grp = g % S;
+  uint32_t* line = wt + grp * kLineWords;     // [0] max, [1] count (one 64-bit word), [2] flag
+  uint32_t* top = wt + kFusedGroups * kLineWords;        // [0] max, [1] count
+  const uint32_t members = (G - grp + S - 1) / S;
+  const uint32_t prev =
+      __hip_atomic_fetch_max(line, wgm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t one;
+  asm volatile("v_mov_b32 %0, 1" : "=v"(one) : "v"(prev));   // waits for the max to return
+  const uint64_t word = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(line),
+                                               (uint64_t)one << 32, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)(word >> 32) == members - 1) {                // this group is complete
+    const uint32_t gm = max((uint32_t)word, wgm);
+    if (S == 1) {                                             // the only group: publish
+      __hip_atomic_store(line + 2, gm | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const uint32_t prev2 =
+          __hip_atomic_fetch_max(top, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t one2;
+      asm volatile("v_mov_b32 %0, 1" : "=v"(one2) : "v"(prev2));
+      const uint64_t word2 = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(top),
+                                                    (uint64_t)one2 << 32, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+      if ((uint32_t)(word2 >> 32) == S - 1) {                 // every group is complete
+        const uint32_t ready = max((uint32_t)word2, gm) | 1u;
+        for (uint32_t i = 0; i < S; ++i)
+          __hip_atomic_store(wt + i * kLineWords + 2, ready, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  uint32_t polls = 0, flag;
+  const uint64_t t0 = wall_clock64();
+  while (!((flag = __hip_atomic_load(line + 2, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT)) & 1u)) {
+    if (polls++ >= wait_polls || wall_clock64() - t0 > wait_ticks) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return (flag & 1u) ? (flag & ~1u) : 0xFFFFFFFFu;
+}
+
 // One tensor t of a fused launch (x = G workgroups of NT threads per tensor): phase 1, the
-// grid-wide wait, phase 2.  nblk <= (KR + KL) * G * NT per tensor and nblk < 2^27 (the host
-// checks both).
-template <int MODE, int RULE, bool FQ, int KR, int KL, int NT>
+// grid-wide wait (the group form when GROUPS, else the collector form), phase 2.
+// nblk <= (KR + KL) * G * NT per tensor, G <= kFusedMaxTensorWGs and nblk < 2^27 (the host
+// checks all three).
+template <int MODE, int RULE, bool FQ, int KR, int KL, int NT, bool GROUPS>
 __device__ __forceinline__ void fused_tensor(
     int64_t t, uint32_t tid, const uint4* __restrict__ in, int64_t nblk,
     uint32_t* __restrict__ ws, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -1019,54 +1154,14 @@ __device__ __forceinline__ void fused_tensor(
   if ((tid & 63) == 0) part[tid >> 6] = m;
   __syncthreads();
 
-  // arrival and the grid-wide wait (one lane), bounded
-  if (tid == 0) {
+  // arrival and the grid-wide wait (wave 0), bounded
+  if (tid < 64) {
     uint32_t wgm = part[0];
     for (int w = 1; w < NT / 64; ++w) wgm = max(wgm, part[w]);
-    // groups of at least 8 workgroups, at most 16 groups; one group needs no top level.  Up
-    // to 16 workgroups meet on one line (measured 11 % faster for the 16-workgroup 256x256
-    // call); 128 workgroups on one line measured 1.5x slower than 16 groups of 8.
-    const uint32_t S = G <= 16u ? 1u : min((uint32_t)kFusedGroups, max(1u, G / 8u));
-    const uint32_t grp = g % S;
     uint32_t* wt = ws + t * kFusedWsWords;
-    uint32_t* line = wt + grp * kLineWords;     // [0] max, [1] count (one 64-bit word), [2] flag
-    uint32_t* top = wt + kFusedGroups * kLineWords;        // [0] max, [1] count
-    const uint32_t members = (G - grp + S - 1) / S;
-    const uint32_t prev =
-        __hip_atomic_fetch_max(line, wgm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t one;
-    asm volatile("v_mov_b32 %0, 1" : "=v"(one) : "v"(prev));   // waits for the max to return
-    const uint64_t word = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(line),
-                                                 (uint64_t)one << 32, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(word >> 32) == members - 1) {                // this group is complete
-      const uint32_t gm = max((uint32_t)word, wgm);
-      if (S == 1) {                                             // the only group: publish
-        __hip_atomic_store(line + 2, gm | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        const uint32_t prev2 =
-            __hip_atomic_fetch_max(top, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t one2;
-        asm volatile("v_mov_b32 %0, 1" : "=v"(one2) : "v"(prev2));
-        const uint64_t word2 = __hip_atomic_fetch_add(reinterpret_cast<uint64_t*>(top),
-                                                      (uint64_t)one2 << 32, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(word2 >> 32) == S - 1) {                 // every group is complete
-          const uint32_t ready = max((uint32_t)word2, gm) | 1u;
-          for (uint32_t i = 0; i < S; ++i)
-            __hip_atomic_store(wt + i * kLineWords + 2, ready, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
-    uint32_t polls = 0, flag;
-    const uint64_t t0 = wall_clock64();
-    while (!((flag = __hip_atomic_load(line + 2, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT)) & 1u)) {
-      if (polls++ >= wait_polls || wall_clock64() - t0 > wait_ticks) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-    amax_sh = (flag & 1u) ? (flag & ~1u) : 0xFFFFFFFFu;   // 0xFFFFFFFF: "compute it here"
+    const uint32_t a = GROUPS ? wait_groups(wt, wgm, g, G, tid, wait_polls, wait_ticks)
+                              : wait_collector(wt, wgm, g, G, tid, wait_polls, wait_ticks);
+    if (tid == 0) amax_sh = a;
   }
   __syncthreads();
   uint32_t abits = amax_sh;
@@ -1133,10 +1228,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT > 256 ? 4
   __shared__ uint4 held[KL > 0 ? KL : 1][2][NT];
   __shared__ uint32_t part[NT / 64];
   __shared__ uint32_t amax_sh;
+  // The wait's form: groups for the 512-thread teams and for the 28-block fake-quant instances,
+  // the collector for every other instance.
+  constexpr bool kGroups = (TEAMS && NT == 512) || (FQ && KR + KL >= 28);
   if (!TEAMS) {
-    fused_tensor<MODE, RULE, FQ, KR, KL, NT>(blockIdx.y, threadIdx.x, in, nblk, ws, codes, scales, out,
-                                         alpha_out, wait_polls, wait_ticks, tb, held, part,
-                                         amax_sh);
+    fused_tensor<MODE, RULE, FQ, KR, KL, NT, kGroups>(blockIdx.y, threadIdx.x, in, nblk, ws, codes,
+                                                    scales, out, alpha_out, wait_polls,
+                                                    wait_ticks, tb, held, part, amax_sh);
     return;
   }
   // Teams that start together stay in step: all load, then all compute, and memory idles while
@@ -1145,7 +1243,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT > 256 ? 4
   // teams loads while the other computes.  The wait is bounded like the grid-wide one; giving
   // up only costs the overlap.  Measured on the 64-expert MoE batch: 445 against 495 us.
   if ((blockIdx.y & 1) && threadIdx.x == 0) {
-    const uint32_t* flag = ws + (blockIdx.y - 1) * kFusedWsWords + 2;
+    const uint32_t* flag =
+        ws + (blockIdx.y - 1) * kFusedWsWords + (kGroups ? 2 : kFlagLine0 * kLineWords);
     const uint64_t t0 = wall_clock64();
     for (uint32_t polls = 0; polls < wait_polls && wall_clock64() - t0 <= wait_ticks &&
          !(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u); ++polls)
@@ -1157,8 +1256,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT > 256 ? 4
     // from hoisting them out of the loop, where they would stay live in registers.
     uint32_t tid;
     asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(threadIdx.x));
-    fused_tensor<MODE, RULE, FQ, KR, KL, NT>(t, tid, in, nblk, ws, codes, scales, out, alpha_out,
-                                         wait_polls, wait_ticks, tb, held, part, amax_sh);
+    fused_tensor<MODE, RULE, FQ, KR, KL, NT, kGroups>(t, tid, in, nblk, ws, codes, scales, out,
+                                                      alpha_out, wait_polls, wait_ticks, tb,
+                                                      held, part, amax_sh);
   }
 }
 
@@ -1492,8 +1592,9 @@ int64_t fused_resident_wgs() {
 // Workgroups per tensor G and teams T for one tier: T = E when every tensor fits on chip at
 // once (TEAMS false), else (TEAMS true) as many teams as are resident together, when at least
 // one is; T = 0 when the tier does not fit.
-//   - An all-at-once tier is taken only with at most kFusedMaxTensorWGs workgroups per tensor:
-//     beyond that the 16 counter lines of the grid-wide wait take more than 32 arrivals each.
+//   - A tensor takes at most kFusedMaxTensorWGs workgroups: the collector form of the wait has
+//     that many slots, and beyond it the 16 counter lines of the group form take more than 32
+//     arrivals each.
 //     Measured on an 8192x4096 tensor, 4/6-MSE packed: the 4-block tier with 2048 workgroups
 //     48.5 us, the 28-block tier with 512 workgroups 34.4 us; rtn6 40.5 against 26.5 us.
 //   - The 12- and 28-block tiers spread each tensor over resident / E workgroups (fewer blocks
@@ -1510,7 +1611,8 @@ int64_t fused_tier_wgs(const Shape& s, int64_t* teams) {
   const int64_t resident = fused_resident_wgs<MODE, RULE, FQ, KR, KL, TEAMS, NT>();
   if (!TEAMS) {
     *teams = (G * s.E <= resident && G <= kFusedMaxTensorWGs) ? s.E : 0;
-    return (KR + KL >= 12 || NT > kThreads) && *teams > 0 ? std::max(G, resident / s.E) : G;
+    return (KR + KL >= 12 || NT > kThreads) && *teams > 0
+               ? std::min(kFusedMaxTensorWGs, std::max(G, resident / s.E)) : G;
   }
   // Teams of the kTeamKR + kTeamKL tier round their size up to a power of two when that still
   // fits four teams and adds at most a quarter: then the two workgroups that share a CU (i and
@@ -1529,9 +1631,9 @@ int64_t fused_tier_wgs(const Shape& s, int64_t* teams) {
       return Gp;
     }
   }
-  const int64_t T = std::min(s.E, resident / G);
+  const int64_t T = G <= kFusedMaxTensorWGs ? std::min(s.E, resident / G) : 0;
   *teams = T;
-  return T > 0 ? std::max(G, resident / T) : G;
+  return T > 0 ? std::min(kFusedMaxTensorWGs, std::max(G, resident / T)) : G;
 }
 
 template <int MODE, int RULE, bool FQ, int KR, int KL, bool TEAMS, int NT>
@@ -1681,7 +1783,7 @@ nvfp4_status run_fused(const uint16_t* in, int64_t E, int64_t rows, int64_t cols
 }  // namespace
 
 // ----------------------------------------------------------------------------- static scratch
-// The allocation-free single-read call keeps the grid-wide wait's counters here instead of
+// The allocation-free single-read call keeps the grid-wide wait's words here instead of
 // in a caller workspace: up to kScratchTensors tensors of NVFP4_FUSED_WS_WORDS words (2176
 // bytes each, 2.1 MiB in all).  Each GPU the library runs on holds its own copy until the
 // process ends.  In host code the array's name is only a stand-in: its device address on a
