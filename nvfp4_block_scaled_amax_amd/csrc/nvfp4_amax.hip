@@ -885,7 +885,12 @@ constexpr int kTeamSmallKR = 10;
 // 349 us, 24x3072x4096 179 against 213 (4 teams of 128, 9 + 4), 96x1024x4096 263 against 265
 // (8 of 64), the others unchanged.  rtn6 and fake-quant output keep the 18 + 2 tier: there the
 // wide tiers measured equal or slower (rtn6 on the MoE batch 352 / 353 / 384 us, rtn6
-// fake-quant 518 / 561 / 528 us, 4/6-MAE fake-quant 547 / 556 / 586 us).
+// fake-quant 518 / 561 / 528 us, 4/6-MAE fake-quant 547 / 556 / 586 us).  (Those figures were
+// taken with the group form of the wait.  With the collector form and Four Over Six loading at
+// the highest issue priority, the two workgroups of a CU settle into opposite phases instead,
+// one computing while the other loads and waits, and the 512-thread teams ran faster again:
+// 64x2048x5120 342 against 378 us, 40x2048x6144 261 against 288, 24x3072x4096 162 against
+// 181, 96x1024x4096 218 against 262.)
 constexpr int kTeamWideKR = 10;
 constexpr int kFusedGroups = 16;
 constexpr int kLineWords = 32;                           // 128 bytes
@@ -1103,6 +1108,12 @@ __device__ __forceinline__ void fused_tensor(
   uint8_t* scalesT = scales + base;
   char* outT = reinterpret_cast<char*>(out + 2 * base);
 
+  // Four Over Six loads at the highest issue priority: a workgroup's loading phase has few
+  // VALU instructions, and when the workgroup sharing its CU is in the block pass (two trials
+  // per block, VALU-bound), they would otherwise wait behind it and delay the arrival of the
+  // whole tensor.  rtn6's block pass is light; there the plain pacing measured faster.
+  constexpr bool kLoadFirst = MODE == NVFP4_FOUR_OVER_SIX;
+  if (kLoadFirst) __builtin_amdgcn_s_setprio(3);
   // phase 1: load every held block (all loads in flight together), magnitude max.  In
   // workgroups of 512 and 1024 threads the blocks held in LDS are loaded straight into it
   // (global_load_lds_dwordx4: each wave writes 1 KB, 16 bytes per lane in lane order, which is
@@ -1185,14 +1196,17 @@ __device__ __forceinline__ void fused_tensor(
   __syncthreads();
   const bool tiny_alpha = alpha < 0x1p-118f;   // 1/d may overflow below 2^-118
   // Phase 2 is bound by the VALU and every workgroup starts it at once: the waves pace
-  // themselves as in quantize_kernel (issue priority 3, 2, 1, 0 by quarters of the held blocks).
+  // themselves as in quantize_kernel, lowering their issue priority by quarters of the held
+  // blocks (3, 2, 1, 0; for Four Over Six 2, 1, 0, 0, below its loading phase).
   constexpr int K = KR + KL;
   constexpr bool pace = K >= (int)kPacedSteps;
-  if (pace) __builtin_amdgcn_s_setprio(3);
+  constexpr int P0 = kLoadFirst ? 2 : 3;
+  if (pace) __builtin_amdgcn_s_setprio(P0);
+  else if (kLoadFirst) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int k = 0; k < KR; ++k) {
-    if (pace && k == K / 4) __builtin_amdgcn_s_setprio(2);
-    if (pace && k == K / 2) __builtin_amdgcn_s_setprio(1);
+    if (pace && k == K / 4) __builtin_amdgcn_s_setprio(P0 - 1);
+    if (pace && k == K / 2) __builtin_amdgcn_s_setprio(P0 - 2 > 0 ? P0 - 2 : 0);
     if (pace && k == (3 * K) / 4) __builtin_amdgcn_s_setprio(0);
     const uint32_t u = ((uint32_t)k * G + g) * NT + tid;
     if (u < n)
@@ -1201,8 +1215,8 @@ __device__ __forceinline__ void fused_tensor(
   }
 #pragma unroll
   for (int k = 0; k < KL; ++k) {
-    if (pace && KR + k == K / 4) __builtin_amdgcn_s_setprio(2);
-    if (pace && KR + k == K / 2) __builtin_amdgcn_s_setprio(1);
+    if (pace && KR + k == K / 4) __builtin_amdgcn_s_setprio(P0 - 1);
+    if (pace && KR + k == K / 2) __builtin_amdgcn_s_setprio(P0 - 2 > 0 ? P0 - 2 : 0);
     if (pace && KR + k == (3 * K) / 4) __builtin_amdgcn_s_setprio(0);
     const uint32_t u = ((uint32_t)(KR + k) * G + g) * NT + tid;
     if (u < n)
@@ -1228,9 +1242,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT > 256 ? 4
   __shared__ uint4 held[KL > 0 ? KL : 1][2][NT];
   __shared__ uint32_t part[NT / 64];
   __shared__ uint32_t amax_sh;
-  // The wait's form: groups for the 512-thread teams and for the 28-block fake-quant instances,
-  // the collector for every other instance.
-  constexpr bool kGroups = (TEAMS && NT == 512) || (FQ && KR + KL >= 28);
+  // The wait's form: groups for the 28-block fake-quant instances (the collector's state does
+  // not fit beside their 224 VGPRs of held blocks), the collector for every other instance.
+  constexpr bool kGroups = FQ && KR + KL >= 28;
   if (!TEAMS) {
     fused_tensor<MODE, RULE, FQ, KR, KL, NT, kGroups>(blockIdx.y, threadIdx.x, in, nblk, ws, codes,
                                                     scales, out, alpha_out, wait_polls,
@@ -1239,7 +1253,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT > 256 ? 4
   }
   // Teams that start together stay in step: all load, then all compute, and memory idles while
   // the VALU works.  Odd teams therefore start when the team before them has published its
-  // first amax (that tensor's ready flag, group 0), half a cycle later, so that one half of the
+  // first amax (that tensor's ready flag), half a cycle later, so that one half of the
   // teams loads while the other computes.  The wait is bounded like the grid-wide one; giving
   // up only costs the overlap.  Measured on the 64-expert MoE batch: 445 against 495 us.
   if ((blockIdx.y & 1) && threadIdx.x == 0) {
@@ -1653,9 +1667,9 @@ void fused_launch(int64_t G, int64_t T, const uint16_t* in, const Shape& s, uint
 
 // Four Over Six teams in 512-thread workgroups, KR + KL blocks per lane (the KL in LDS, loaded
 // straight into it), in teams of a power-of-two number of workgroups: then the two workgroups
-// that share a CU (i and i + #CUs) belong to teams y and y + T/2, which the odd/even start
-// puts in the same phase.  Taken when at least four such teams fit; returns whether it was
-// (and launches when asked).
+// that share a CU (i and i + #CUs) belong to teams y and y + T/2, and every CU holds the same
+// pair of teams.  Taken when at least four such teams fit; returns whether it was (and
+// launches when asked).
 template <int MODE, int RULE, bool FQ, int KR, int KL>
 bool fused_team512(bool launch, const uint16_t* in, const Shape& s, uint32_t* ws,
                    uint8_t* codes, uint8_t* scales, float* alpha, hipStream_t stream) {
