@@ -197,17 +197,48 @@ def test_fused_teams_whole_batch(nv, orc, shape, mode, rule, fq):
     assert_matches_oracle(orc, x, run_fused(nv, x, mode, rule, fq), mode, rule, fq, str(shape))
 
 
-@pytest.mark.parametrize("limit", [0, 1], ids=["never-wait", "one-poll"])
-def test_fused_teams_bounded_wait(nv, orc, limit):
-    shape = (6, 1024, 16384)
+def check_limits(nv, orc, x, mode, rule, fq, tag):
+    """The call with the wait cut short from the host (no poll, then one poll), against one
+    oracle result: workgroups that stop waiting compute the tensor amax alone."""
+    ref = orc.quantize(x, mode, rule, nthreads=NTHREADS, want_y=fq)
+    E = x.shape[0] if x.ndim == 3 else 1
+    for limit in (0, 1):
+        nv.set_fused_wait_limit(limit)
+        try:
+            say("[fused] %s wait limit %d" % (tag, limit))
+            got = run_fused(nv, x, mode, rule, fq)
+        finally:
+            nv.set_fused_wait_limit(-1)
+        assert np.array_equal(got["alpha"].view(np.uint32), ref["alpha"][:E].view(np.uint32)), (tag, limit)
+        if fq:
+            assert np.array_equal(got["y"], ref["y"]), (tag, limit)
+        else:
+            assert np.array_equal(got["codes"], ref["codes"]), (tag, limit)
+            assert np.array_equal(got["scales"], ref["scales"]), (tag, limit)
+
+
+# Team launches of each kind with the wait cut short: 1024-thread teams, 512-thread teams (the
+# Four Over Six loading phase at raised issue priority), teams of the small-tensor tier.
+TEAM_LIMITS = [((6, 1024, 16384), "four_over_six", "mse", False, 10),
+               ((16, 1024, 4096), "four_over_six", "mse", False, 10),
+               ((600, 256, 256), "four_over_six", "mae", True, 10)]
+
+
+@pytest.mark.parametrize("shape,mode,rule,fq,tier", TEAM_LIMITS,
+                         ids=["teams1024", "teams512", "small-teams"])
+def test_fused_teams_bounded_wait(nv, orc, shape, mode, rule, fq, tier):
+    assert nv.fused_blocks_per_lane(shape, mode, rule, fq) == tier
     x = W.bits(W.generate("moe", shape))
-    nv.set_fused_wait_limit(limit)
-    try:
-        say("[fused-teams] wait limit %d" % limit)
-        assert_matches_oracle(orc, x, run_fused(nv, x, "four_over_six", "mse", False),
-                              "four_over_six", "mse", False, "teams-limit%d" % limit)
-    finally:
-        nv.set_fused_wait_limit(-1)
+    check_limits(nv, orc, x, mode, rule, fq, "teams %s" % (shape,))
+
+
+def test_fused_group_wait_bounded(nv, orc):
+    """The 28-block fake-quant tier meets at the two-level counter (the other instances use one
+    collector workgroup); its bounded wait falls back the same way."""
+    shape = (4096, 14336)
+    assert nv.fused_blocks_per_lane(shape, "four_over_six", "mae", True) == 28
+    x = W.bits(W.weight(shape, seed=401))
+    check_limits(nv, orc, x, "four_over_six", "mae", True, "group-form")
 
 
 def test_fused_teams_moe_full_size(nv, orc):
