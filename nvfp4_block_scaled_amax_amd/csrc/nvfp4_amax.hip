@@ -161,6 +161,44 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restr
   }
 }
 
+// Blocks scaled to 4 per tensor, counted from the per-block choice bytes (4 or 6; 0 for a
+// poisoned tensor): count4[t] += the bytes equal to 4 in qstar[t * nblk, (t + 1) * nblk).
+// Grid: x = workgroups per tensor, y = tensor.  The 16-byte-aligned middle of the range is read
+// in 16-byte chunks, the at most 15 bytes before and after it one by one; one atomic per
+// workgroup.
+__global__ __launch_bounds__(kThreads) void count4_kernel(const uint8_t* __restrict__ qstar,
+                                                          int64_t nblk,
+                                                          uint32_t* __restrict__ count4) {
+  const int64_t t = blockIdx.y;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(qstar) + (uintptr_t)(t * nblk);
+  const uintptr_t hi = lo + (uintptr_t)nblk;
+  const uintptr_t a = std::min((lo + 15) & ~(uintptr_t)15, hi);
+  const uintptr_t b = std::max(a, hi & ~(uintptr_t)15);
+  const uint4* q = reinterpret_cast<const uint4*>(a);
+  const int64_t chunks = (int64_t)((b - a) >> 4);
+  uint32_t c = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks;
+       i += (int64_t)gridDim.x * kThreads) {
+    const uint4 v = q[i];   // a byte is 4 when its bit 2 is set and its bit 1 clear
+    c += __popc(v.x & ~(v.x << 1) & 0x04040404u) + __popc(v.y & ~(v.y << 1) & 0x04040404u) +
+         __popc(v.z & ~(v.z << 1) & 0x04040404u) + __popc(v.w & ~(v.w << 1) & 0x04040404u);
+  }
+  if (blockIdx.x == 0 && threadIdx.x < 32) {
+    const uintptr_t j = threadIdx.x < 16 ? lo + threadIdx.x : b + (threadIdx.x - 16);
+    if (j < (threadIdx.x < 16 ? a : hi) && *reinterpret_cast<const uint8_t*>(j) == 4) ++c;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+  __shared__ uint32_t wsum[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+    for (int w = 0; w < kThreads / 64; ++w) tot += wsum[w];
+    if (tot) atomicAdd(count4 + t, tot);
+  }
+}
+
 __global__ void alpha_kernel(const uint32_t* amax_bits, float* alpha,
                              int64_t E, float C) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -708,7 +746,8 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
       }
     }
   }
-  if (DIAG) {            // one integer atomic per workgroup: exact, order-free
+  if (DIAG && count4) {  // blocks scaled to 4: one integer atomic per workgroup, exact and
+                         // order-free (long plain diagnostics launches count qstar afterwards)
     __shared__ uint32_t wsum[kThreads / 64];
     uint32_t v = n_four;
 #pragma unroll
@@ -1390,10 +1429,16 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
   // statistics workspace: E counter lines, then the slots (reused by consecutive launches)
   double* const slots = stats_ws ? reinterpret_cast<double*>(stats_ws + s.E * kDiagCtrWords)
                                  : nullptr;
+  // The diagnostics count the blocks scaled to 4 with one atomic per workgroup, which keeps
+  // their grid at kDiagLaunchWGs workgroups.  A long plain diagnostics call instead takes the
+  // block pass's grid and counts the choice bytes afterwards (count4_kernel): the 64-expert MoE
+  // batch 538 against 595 us (4/6-MSE) and 522 against 605 (rtn6); short calls measured up to
+  // 7 % slower that way (the weight: 58.1 against 55.0 us), so they keep the atomic.
+  const bool count_after = DIAG == kDiagPlain && s.E * s.nblk >= kLongLaunchBlocks;
   auto launch = [&](int64_t E, int64_t nblk, int64_t first_tensor, int64_t first_block) {
     const int64_t one_per_lane = (nblk + kThreads - 1) / kThreads;
     int64_t per_tensor = one_per_lane;
-    if (DIAG)
+    if (DIAG && !count_after)
       per_tensor = std::min(one_per_lane, std::max<int64_t>(1, kDiagLaunchWGs / E));
     else if (MODE == NVFP4_FOUR_OVER_SIX && !FQ)
       per_tensor = E * nblk < kLongLaunchBlocks
@@ -1407,7 +1452,7 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
                        scales ? scales + b0 : nullptr,
                        reinterpret_cast<uint4*>(out ? out + b0 * 16 : nullptr),
                        alpha_out ? alpha_out + first_tensor : nullptr, qstar ? qstar + b0 : nullptr,
-                       count4 ? count4 + first_tensor : nullptr,
+                       count4 && !count_after ? count4 + first_tensor : nullptr,
                        stats ? stats + first_tensor * NVFP4_NSTATS : nullptr,
                        stats ? stats_ws + first_tensor * kDiagCtrWords : nullptr,
                        stats ? slots : nullptr);
@@ -1418,6 +1463,13 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
     for (int64_t t = 0; t < s.E; ++t)
       for (int64_t b = 0; b < s.nblk; b += kMaxLaunchBlocks)
         launch(1, std::min(kMaxLaunchBlocks, s.nblk - b), t, b);
+  }
+  if (count_after) {        // 16-byte chunks per tensor, 16 per lane, up to kDiagLaunchWGs WGs
+    const int64_t per_tensor = std::max<int64_t>(
+        1, std::min<int64_t>(std::max<int64_t>(1, kDiagLaunchWGs / s.E),
+                             (s.nblk + 16 * 16 * kThreads - 1) / (16 * 16 * kThreads)));
+    hipLaunchKernelGGL(count4_kernel, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kThreads),
+                       0, stream, qstar, s.nblk, count4);
   }
 }
 

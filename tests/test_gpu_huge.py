@@ -2,7 +2,8 @@
 
 Block indices inside a kernel are 32-bit, so the host splits the block pass of a tensor with
 2^27 blocks or more into launches over consecutive block ranges (offset pointers, one tensor
-per launch).  This runs the dynamic packed, fake-quant and diagnostics calls on a
+per launch).  This runs the dynamic packed, fake-quant and diagnostics calls (with and
+without statistics) on a
 131080 x 16384 bf16 tensor (2^27 + 8192 blocks, 4.3 GB) and compares the whole packed output,
 alpha, the count of blocks scaled to 4, the error statistics (summed over both launches), and
 sampled fake-quant and dequantized blocks around the launch boundary with the oracle
@@ -53,6 +54,11 @@ def test_tensor_over_2pow27_blocks(nv, orc):
     cq, sq, aq, q, n4, stg = nv.quantize_diag(xg, "four_over_six", "mse")
     torch.cuda.synchronize()
     assert torch.equal(cq, c) and torch.equal(sq, s) and torch.equal(aq, a)
+    say("[huge] diagnostics without statistics (counted from the choice bytes after the pass)")
+    cp, sp, ap, qp, n4p, _ = nv.quantize_diag(xg, "four_over_six", "mse", stats=False)
+    torch.cuda.synchronize()
+    assert torch.equal(cp, c) and torch.equal(sp, s) and torch.equal(qp, q) and torch.equal(n4p, n4)
+    del cp, sp, qp
     codes, scales = c.cpu().numpy(), s.cpu().numpy()
     qstar_gpu, n4_gpu, stats_gpu = q.cpu().numpy(), int(n4.cpu()[0]), stg.cpu().numpy()
     del cq, sq, q

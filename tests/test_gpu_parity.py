@@ -501,6 +501,45 @@ def test_diag_poison_and_edges(nv, orc):
     assert np.isnan(st.cpu().numpy()).sum() == 0
 
 
+@pytest.mark.parametrize("shape", [(2, 1, 16), (5, 3, 112), (7, 40, 176), (3000, 48)],
+                         ids=["one-block-tensors", "21-blocks", "440-blocks", "one-tensor"])
+def test_diag_count_from_choice_bytes(nv, orc, shape):
+    """Without statistics the count of blocks scaled to 4 comes from the per-block choice bytes
+    after the pass: tensors whose byte ranges start and end off 16-byte boundaries, and a
+    poisoned tensor (choice bytes 0, count 0)."""
+    x = W.bits(W.generate("moe", shape) if len(shape) == 3 else W.weight(shape, seed=43)).copy()
+    if x.ndim == 3:
+        x[1, 0, 3] = 0x7FC0
+    c, s, a, q, n4, st = nv.quantize_diag(to_gpu(x), "four_over_six", "mse", stats=False)
+    torch.cuda.synchronize()
+    ref = orc.quantize(x, "four_over_six", "mse", want_y=False, want_qstar=True)
+    E = x.shape[0] if x.ndim == 3 else 1
+    assert np.array_equal(q.cpu().numpy(), ref["qstar"])
+    assert np.array_equal(n4.cpu().numpy(), (ref["qstar"].reshape(E, -1) == 4).sum(axis=1))
+    assert np.array_equal(c.cpu().numpy(), ref["codes"])
+    if x.ndim == 3:
+        assert n4.cpu().numpy()[1] == 0 and (q.cpu().numpy()[1] == 0).all()
+
+
+def test_diag_count_long_call(nv, orc):
+    """A plain diagnostics call of 2^23 blocks or more takes the block pass's grid and counts
+    the choice bytes after the pass: five tensors of 1,678,677 blocks (an odd count, so every
+    tensor's byte range starts and ends off a 16-byte boundary), one of them poisoned."""
+    shape = (5, 1001, 26832)
+    x = W.bits(W.generate("moe", shape)).copy()
+    x[2, 500, 7] = 0xFF80            # -inf
+    assert x.size // 16 >= 2 ** 23 and (x.size // 16 // 5) % 16 != 0
+    c, s, a, q, n4, _ = nv.quantize_diag(to_gpu(x), "four_over_six", "mse", stats=False)
+    torch.cuda.synchronize()
+    ref = orc.quantize(x, "four_over_six", "mse", nthreads=NTHREADS, want_y=False,
+                       want_qstar=True)
+    assert np.array_equal(q.cpu().numpy(), ref["qstar"])
+    want = (ref["qstar"].reshape(5, -1) == 4).sum(axis=1)
+    assert np.array_equal(n4.cpu().numpy(), want) and want[2] == 0 and want.sum() > 0
+    assert np.array_equal(c.cpu().numpy(), ref["codes"])
+    assert np.array_equal(s.cpu().numpy(), ref["scales"])
+
+
 @pytest.mark.parametrize("shape", [(1024, 8208), (4, 300, 640), (1100, 2, 32)],
                          ids=["one-tensor", "batched", "more-tensors-than-slots"])
 def test_diag_stats_repeatable_with_any_workspace(nv, orc, shape):
