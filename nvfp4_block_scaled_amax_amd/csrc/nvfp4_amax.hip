@@ -1216,6 +1216,10 @@ __device__ __forceinline__ void fused_tensor(
       }
     }
   }
+  // Every load is issued before the first use of a loaded register: the compiler waits for
+  // all outstanding loads at such a use once LDS-bound loads are among them, so a use
+  // scheduled between the loads would hold back the loads after it by a whole round trip.
+  if constexpr (kDma) __builtin_amdgcn_sched_barrier(0);
   uint32_t m = 0;
 #pragma unroll
   for (int k = 0; k < KR; ++k) m = mag_max8(mag_max8(m, r0[k]), r1[k]);
