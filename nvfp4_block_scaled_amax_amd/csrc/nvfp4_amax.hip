@@ -126,28 +126,47 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Grid: x = workgroups per tensor, y = tensor.  Few, large workgroups (one atomic each:
 // same-address atomics serialize, so their count is kept near the CU count).  Each lane
-// reads C consecutive 16-byte chunks per step, the workgroups striding over the tensor:
-// C = 8 (128 bytes, 64 bf16 values) when that still gives every tensor its share of the
-// workgroups, else C = 1 so that small tensors spread over more CUs.
+// reads C 16-byte chunks per step, the workgroups striding over the tensor: C = 8 (64 bf16
+// values) when that still gives every tensor its share of the workgroups, else C = 1 so that
+// small tensors spread over more CUs.  The C chunks are consecutive (128 bytes per lane), or
+// with COAL 1024 chunks apart, so that each load instruction of a wave reads 1 KB contiguous.
 constexpr int kAmaxThreads = 1024;
 constexpr int kAmaxWGs = 256;
-template <int C>
+template <int C, bool COAL>
 __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint4* __restrict__ in,
                                                             int64_t chunks,
                                                             uint32_t* __restrict__ acc) {
   const uint4* p = in + (int64_t)blockIdx.y * chunks;
-  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads * C;
-  int64_t i = ((int64_t)blockIdx.x * kAmaxThreads + threadIdx.x) * C;
   uint32_t m = 0;
-  for (; i + C <= chunks; i += stride) {
-    uint4 v[C];
+  if (COAL) {     // a workgroup's step is C * 1024 consecutive chunks, 1 KB per load instruction
+    const int64_t span = (int64_t)kAmaxThreads * C;
+    const int64_t stride = (int64_t)gridDim.x * span;
+    int64_t b = (int64_t)blockIdx.x * span;
+    for (; b + span <= chunks; b += stride) {
+      uint4 v[C];
 #pragma unroll
-    for (int k = 0; k < C; ++k) v[k] = p[i + k];
+      for (int k = 0; k < C; ++k) v[k] = p[b + k * kAmaxThreads + threadIdx.x];
 #pragma unroll
-    for (int k = 0; k < C; ++k) m = mag_max8(m, v[k]);
+      for (int k = 0; k < C; ++k) m = mag_max8(m, v[k]);
+    }
+    if (b < chunks)                                // the one span that runs past the end
+      for (int k = 0; k < C; ++k) {
+        const int64_t j = b + k * kAmaxThreads + threadIdx.x;
+        if (j < chunks) m = mag_max8(m, p[j]);
+      }
+  } else {
+    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads * C;
+    int64_t i = ((int64_t)blockIdx.x * kAmaxThreads + threadIdx.x) * C;
+    for (; i + C <= chunks; i += stride) {
+      uint4 v[C];
+#pragma unroll
+      for (int k = 0; k < C; ++k) v[k] = p[i + k];
+#pragma unroll
+      for (int k = 0; k < C; ++k) m = mag_max8(m, v[k]);
+    }
+    if (C > 1)
+      for (; i < chunks; ++i) m = mag_max8(m, p[i]);   // the one lane whose chunks run past the end
   }
-  if (C > 1)
-    for (; i < chunks; ++i) m = mag_max8(m, p[i]);   // the one lane whose chunks run past the end
   // the larger of the two 16-bit magnitudes, as the bits of a binary32 value
   m = max(m & 0xFFFFu, m >> 16) << 16;
   m = wave_max_u32(m);
@@ -1442,15 +1461,29 @@ hipError_t launch_amax(const uint16_t* in, const Shape& s, uint32_t* acc, hipStr
   const int64_t want8 = (chunks + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
   const int64_t want1 = (chunks + kAmaxThreads - 1) / kAmaxThreads;
   const bool wide = want8 >= share;
-  const int64_t per_tensor = std::max<int64_t>(1, std::min<int64_t>(wide ? want8 : want1, share));
+  // wide: as few workgroups as keep the steps per lane at ceil(want8 / share), so that no
+  // workgroup runs a last step that the others do not
+  // (4096x14336: 224 workgroups of 4 steps, 23.31 against 23.81 us for 256 of 3.5 steps)
+  const int64_t per_tensor =
+      wide ? (want8 + (want8 + share - 1) / share - 1) / ((want8 + share - 1) / share)
+           : std::max<int64_t>(1, std::min<int64_t>(want1, share));
   const int64_t nclear = std::max({s.E, acc3 ? n3 : 0, acc4 ? n4 : 0});
   hipLaunchKernelGGL(clear_kernel, dim3((unsigned)((nclear + kThreads - 1) / kThreads)), dim3(kThreads),
                      0, stream, acc, acc2, s.E, acc3, n3, acc4, n4);
-  if (wide)
-    hipLaunchKernelGGL(amax_kernel<8>, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
+  // A single tensor of at most 8 steps per lane reads coalesced (each load instruction 1 KB
+  // contiguous); longer tensors and batches read 128 contiguous bytes per lane.  Same-box A/B,
+  // median of 6 rounds: 4096x14336 22.72 against 23.27 us, 8192x4096 15.54 against 16.12, but
+  // 16384x14336 (14 steps) 78.93 against 77.10; an earlier A/B found the 64-expert batch
+  // 227.4 against 217.4 coalesced.
+  const bool coalesced = wide && s.E == 1 && want8 <= 8 * share;
+  if (coalesced)
+    hipLaunchKernelGGL((amax_kernel<8, true>), dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
+                       0, stream, reinterpret_cast<const uint4*>(in), chunks, acc);
+  else if (wide)
+    hipLaunchKernelGGL((amax_kernel<8, false>), dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
                        0, stream, reinterpret_cast<const uint4*>(in), chunks, acc);
   else
-    hipLaunchKernelGGL(amax_kernel<1>, dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
+    hipLaunchKernelGGL((amax_kernel<1, false>), dim3((unsigned)per_tensor, (unsigned)s.E), dim3(kAmaxThreads),
                        0, stream, reinterpret_cast<const uint4*>(in), chunks, acc);
   return hipGetLastError();
 }
