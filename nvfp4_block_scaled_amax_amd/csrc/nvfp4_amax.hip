@@ -238,8 +238,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //   - rtn6 and fake-quant are light per block and run fastest with one block per lane and as
 //     many waves as fit: 5-17 % faster than a fixed 1024 workgroups.
 //   - Four Over Six into packed output (two trials per block) needs its own loads in flight
-//     across its arithmetic.  Below 2^23 blocks (268 MB of input) 1024 workgroups in all
-//     (about 14 blocks per lane for the 4096x14336 weight) beat 4 blocks per lane by 3-5 %;
+//     across its arithmetic.  Below 2^23 blocks (268 MB of input) a fixed grid (1024
+//     workgroups, 14 blocks per lane for the 4096x14336 weight) beat 4 blocks per lane by 3-5 %;
 //     from 2^23 blocks on, 4 blocks per lane beat 1024 or 768 workgroups by 4-12 % (MoE 10 %),
 //     and 3 blocks per lane beat 4 in four same-box A/B runs on three boxes: the 64-expert MoE
 //     batch 293.7-298.4 against 299.6-304.0 us, the 16384x14336 tensor 107.5-109.1 against
@@ -251,9 +251,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //   2048 workgroups, 8 or 16 blocks per lane, 2048 or 4096 workgroups for long launches, and
 //   1024-4096 workgroups for rtn6 and fake-quant were all slower or equal.  With the first loads issued
 //   at the kernel's start, 768, 1536 and 2048 workgroups measured 1-7 % slower than 1024 on
-//   the 4096x14336 weight.
+//   the 4096x14336 weight.  With the outputs stored one step late, 768 workgroups (3 per CU)
+//   overtook 1024 (4 per CU) below 2^23 blocks in three same-box A/B runs: the 4096x14336
+//   weight 28.51 against 29.00 us (MSE) and 28.42 against 29.12 (MAE), 28.41 against 29.04 on
+//   another box, the 8192x4096 activation packed 17.31 against 17.40; 512 and 896 workgroups
+//   were slower than both (30.10 and 30.16 us on the weight).
 constexpr int64_t kLongLaunchBlocks = INT64_C(1) << 23;
-constexpr int64_t kShortLaunchWGs = 1024;
+constexpr int64_t kShortLaunchWGs = 768;
 constexpr int64_t kLaneBlocksLong = 3;
 constexpr int64_t kDiagLaunchWGs = 1024;
 constexpr uint32_t kPacedSteps = 8;      // grid-stride steps per lane from which waves pace themselves
