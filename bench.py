@@ -24,8 +24,9 @@ Timing:
     (the amax pass reads the input a second time: 4.5625 or 6 B/elem) are
     reported separately as hbm_bytes_per_step.
   * per-kernel legs: graphs of back-to-back launches of one pass over rotating
-    cold buffers, HIP events recorded on the launch stream before and after the
-    replay; the average launch of the block pass is the roofline figure.  Also
+    cold buffers, one untimed replay, then HIP events recorded on the launch stream
+    before and after each of 5 replays; the average launch of the block pass is the
+    roofline figure.  Also
     timed this way: the rtn6 block pass, the amax pass, the two-pass and the
     single-read dynamic calls, the diagnostics call (with and without error
     statistics) and dequantize (packed -> bf16).
@@ -243,8 +244,10 @@ def main():
         return g
 
     def replay_us(g, count, reps=5):
-        """(events around one replay) / count in microseconds, over reps replays:
-        (median, min, max)."""
+        """(events around one replay) / count in microseconds, over reps replays after one
+        untimed replay: (median, min, max)."""
+        g.replay()
+        torch.cuda.synchronize()
         out = []
         for _ in range(reps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
