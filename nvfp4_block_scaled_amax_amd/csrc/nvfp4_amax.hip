@@ -738,11 +738,12 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   const bool pace = steps >= kPacedSteps && (!DIAG || want_stats);
   const uint32_t q1 = steps / 4, q2 = steps / 2, q3 = (3 * steps) / 4;
   // Each block's outputs are stored one step late, right after the wait for the step's loads.
-  // On this chip one counter (vmcnt) tracks loads and stores alike, and the compiler takes
-  // loads and stores as completing in any order, so the wait for the prefetched block waits for
-  // every store issued before it.  Stored at the end of their own step, a block's outputs made
-  // the next step wait for their write to complete; stored one step late, they have a whole
-  // step to complete, like the prefetch.  Measured against stores at the end of the step (same
+  // On this chip one counter (vmcnt) tracks loads and stores alike.  With the stores at the
+  // end of their own step, the compiler's wait at the top of the next step came out as
+  // vmcnt(0) (the loop header joins the entry path and the back edge, and the loop calls the
+  // reference path), so the wait for the prefetched block also waited for the stores just
+  // issued.  Stored one step late, after the vmcnt(0) that the step needs anyway for its
+  // prefetched block, they have a whole step to complete, like the prefetch.  Measured against stores at the end of the step (same
   // box, A/B, two boxes): Four Over Six packed 2-3 % faster (the weight 28.9 against 29.8 us,
   // the large tensor 106.2 against 108.8, the MoE batch 288.3-294.3 against 296.6-299.0); rtn6
   // and fake-quant equal; the diagnostics call within -3.5 to +0.8 %.
