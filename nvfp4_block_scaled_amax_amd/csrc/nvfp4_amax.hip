@@ -743,10 +743,11 @@ __attribute__((amdgpu_waves_per_eu(NVFP4_WAVES_PER_EU))) void quantize_kernel(
   // vmcnt(0) (the loop header joins the entry path and the back edge, and the loop calls the
   // reference path), so the wait for the prefetched block also waited for the stores just
   // issued.  Stored one step late, after the vmcnt(0) that the step needs anyway for its
-  // prefetched block, they have a whole step to complete, like the prefetch.  Measured against stores at the end of the step (same
-  // box, A/B, two boxes): Four Over Six packed 2-3 % faster (the weight 28.9 against 29.8 us,
-  // the large tensor 106.2 against 108.8, the MoE batch 288.3-294.3 against 296.6-299.0); rtn6
-  // and fake-quant equal; the diagnostics call within -3.5 to +0.8 %.
+  // prefetched block, they have a whole step to complete, like the prefetch.  Measured
+  // against stores at the end of the step (same box, A/B, two boxes): Four Over Six packed
+  // 2-3 % faster (the weight 28.9 against 29.8 us, the large tensor 106.2 against 108.8, the
+  // MoE batch 288.3-294.3 against 296.6-299.0); rtn6 and fake-quant equal; the diagnostics
+  // call within -3.5 to +0.8 %.
   uint32_t pu = 0;                                     // the block held back, and its outputs:
   uint32_t py[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};   // fake-quant words, or codes, scale, Q*
   if (pace) __builtin_amdgcn_s_setprio(3);
