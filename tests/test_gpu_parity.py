@@ -170,10 +170,14 @@ def test_amax_matches_oracle(nv, orc):
         assert np.array_equal(got.view(np.uint32), orc.amax(x, E).view(np.uint32)), name
 
 
-# Both amax variants (8 chunks per lane step for tensors that fill their workgroups, 1 chunk
-# otherwise), tensors whose chunk count is not a multiple of 8 (the 8-chunk variant's tail
-# lane), and the maximum planted first, last and in the middle of each tensor.
-AMAX_SHAPES = [(1, 16), (7, 48), (2049, 8208), (3, 1000, 5136), (3, 1001, 5648), (300, 2, 32)]
+# Every amax variant: 8 chunks per lane step for tensors that fill their workgroups, read
+# coalesced for a single tensor of at most 8 steps per lane (2049x8208: 129 workgroups of 2
+# steps, the last span running past the end) and 128 contiguous bytes per lane for longer
+# single tensors (8193x16400: 228 workgroups of 9 steps) and batches (3x1001x5648); 1 chunk
+# otherwise.  Chunk counts that are not a multiple of 8 (the tail lane of the 128-byte form),
+# and the maximum planted first, last and in the middle of each tensor.
+AMAX_SHAPES = [(1, 16), (7, 48), (2049, 8208), (8193, 16400), (3, 1000, 5136), (3, 1001, 5648),
+               (300, 2, 32)]
 
 
 @pytest.mark.parametrize("shape", AMAX_SHAPES, ids=["x".join(map(str, s)) for s in AMAX_SHAPES])
