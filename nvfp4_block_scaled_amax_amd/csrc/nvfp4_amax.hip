@@ -246,7 +246,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 //     109.5-110.3 us.  (2 per lane: faster than 3 on the 16384x14336 tensor in one run and
 //     slower on the MoE batch in another; 6 and 8: 4-10 % slower.)
 //   - The diagnostics variant ends with one or two same-address atomics per workgroup (the
-//     count of blocks scaled to 4, the statistics counter): 1024 workgroups in all.
+//     count of blocks scaled to 4, the statistics counter): 1024 workgroups in all with
+//     statistics (one workspace slot each); without, the block pass's 768 (same-box A/B: the
+//     8192x4096 activation 37.64 against 39.67 us, the 4096x14336 weight 52.76 against 53.37).
 //   With paced waves (see the block-pass loop) the choices were measured again: 768, 1536 or
 //   2048 workgroups, 8 or 16 blocks per lane, 2048 or 4096 workgroups for long launches, and
 //   1024-4096 workgroups for rtn6 and fake-quant were all slower or equal.  With the first loads issued
@@ -1512,8 +1514,10 @@ void launch_quantize_t(const uint16_t* in, const Shape& s, const float* amax, ui
   auto launch = [&](int64_t E, int64_t nblk, int64_t first_tensor, int64_t first_block) {
     const int64_t one_per_lane = (nblk + kThreads - 1) / kThreads;
     int64_t per_tensor = one_per_lane;
-    if (DIAG && !count_after)
-      per_tensor = std::min(one_per_lane, std::max<int64_t>(1, kDiagLaunchWGs / E));
+    if (DIAG && !count_after)   // the statistics need their kDiagLaunchWGs workspace slots
+      per_tensor = std::min(one_per_lane,
+                            std::max<int64_t>(1, (DIAG == kDiagPlain ? kShortLaunchWGs
+                                                                      : kDiagLaunchWGs) / E));
     else if (MODE == NVFP4_FOUR_OVER_SIX && !FQ)
       per_tensor = E * nblk < kLongLaunchBlocks
                        ? std::min(one_per_lane, std::max<int64_t>(1, kShortLaunchWGs / E))
